@@ -1,0 +1,156 @@
+"""Pins for the cascade (modded-nanogpt anvil.py, `anvil_cascade` tall and wide branches and the
+table of six quintic maps).
+
+The spectral pin: for X = U S V^T, A = V S^2 V^T (tall) or U S^2 U^T (wide), so B is a polynomial
+in A and each map sends every singular value s to a s + b s^3 + c s^5 while keeping U and V.
+After the normalisation by d the whole cascade is therefore U F(S/d) V^T with F the composition of
+the six scalar quintics.  numpy's SVD is the independent witness.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import anvil_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "rounding_points.json")
+
+
+def F(s):
+    s = np.asarray(s, dtype=np.float64)
+    for a, b, c in O.ANVIL_MAPS:
+        s = a * s + b * s ** 3 + c * s ** 5
+    return s
+
+
+def _svd_expect(X):
+    U, S, Vt = np.linalg.svd(X, full_matrices=False)
+    d = np.sqrt(np.sum(X ** 2)) * 1.05 + 1e-6
+    return (U * F(S / d)[None, :]) @ Vt
+
+
+@pytest.mark.parametrize("shape", [(8, 24), (24, 8), (16, 16), (64, 48), (48, 64), (5, 5), (1, 9), (9, 1)])
+def test_exact_mode_equals_svd_closed_form(shape):
+    rng = np.random.default_rng(sum(shape))
+    X = rng.standard_normal(shape)
+    got = O.cascade(X[None], exact=True)[0]
+    want = _svd_expect(X)
+    if min(shape) == 1:
+        # rank one: sigma/d = 1/1.05 (minus eps), at the edge of the maps' window; F is steep
+        # there, so compare at a looser tolerance
+        np.testing.assert_allclose(got, want, rtol=1e-6, atol=1e-9)
+    else:
+        np.testing.assert_allclose(got, want, rtol=1e-9, atol=1e-12)
+
+
+def test_composite_map_window():
+    """F (from the six tabulated maps) sends [0.003, 0.95] into [0.99, 1.01] and [0.0013, 0.95]
+    into [0.7, 1.3]; it blows up just above 1/1.05."""
+    s = np.linspace(0.003, 0.95, 20001)
+    assert np.max(np.abs(F(s) - 1)) <= 0.01
+    s = np.linspace(0.0013, 0.95, 20001)
+    assert np.all((F(s) >= 0.7) & (F(s) <= 1.3))
+    assert F(0.96) > 10
+
+
+def test_bf16_mode_tracks_closed_form():
+    rng = np.random.default_rng(11)
+    for shape in [(96, 40), (40, 96), (64, 64), (1100, 24)]:
+        X = O.R(rng.standard_normal(shape).astype(np.float32))
+        got = O.cascade(X[None])[0].astype(np.float64)
+        want = _svd_expect(X.astype(np.float64))
+        rel = np.linalg.norm(got - want) / np.linalg.norm(want)
+        assert rel < 1.5e-2, (shape, rel)
+        sv = np.linalg.svd(got, compute_uv=False)
+        assert np.all(np.abs(sv - 1) <= 0.3), (shape, sv.min(), sv.max())
+
+
+@pytest.mark.parametrize("split", [False, True])
+def test_transpose_symmetry_bit_exact(split):
+    """The wide branch on X^T is the transpose of the tall branch on X (same split flag)."""
+    rng = np.random.default_rng(12)
+    X = O.R(rng.standard_normal((2, 72, 40)).astype(np.float32))
+    tall = O.cascade(X, split=split)
+    wide = O.cascade(np.swapaxes(X, 1, 2).copy(), split=split)
+    assert np.array_equal(tall, np.swapaxes(wide, 1, 2))
+
+
+def test_split_and_fused_rounding_golden():
+    g = json.load(open(GOLDEN))
+    c = g["apply_tall"]
+    X = np.array(c["X"], np.float32)[None]
+    B = np.array(c["B"], np.float32)[None]
+    assert np.array_equal(O.apply(X, B, c["a"], tall=True, split=True)[0], np.array(c["split"], np.float32))
+    assert np.array_equal(O.apply(X, B, c["a"], tall=True, split=False)[0], np.array(c["fused"], np.float32))
+    # wide form on the transposed operands
+    Xt = np.swapaxes(X, 1, 2).copy()
+    assert np.array_equal(O.apply(Xt, B, c["a"], tall=False, split=True)[0].T, np.array(c["split"], np.float32))
+    p = g["poly"]
+    A = np.array(p["A"], np.float32)[None]
+    assert np.array_equal(O.poly(A, p["b"], p["c"])[0], np.array(p["B"], np.float32))
+
+
+def test_zero_gradient_gives_zero_update():
+    G = np.zeros((2, 48, 16), np.float32)
+    v = np.zeros((2, 2, 48, 16), np.float32)
+    out, v2 = O.bank_step(G, v, 0.95, 0.85, 1.0)
+    assert np.all(out == 0)
+    assert np.all(v2 == 0)
+
+
+def test_nan_propagates():
+    rng = np.random.default_rng(13)
+    G = rng.standard_normal((2, 24, 16)).astype(np.float32)
+    G[1, 3, 4] = np.nan
+    v = np.zeros((2, 2, 24, 16), np.float32)
+    out, _ = O.bank_step(G, v, 0.95, 0.85, 1.0)
+    f = O.bf16_to_f32(out)
+    assert np.all(np.isfinite(f[0]))
+    assert np.all(np.isnan(f[1]))
+
+
+def test_batch_invariance():
+    rng = np.random.default_rng(14)
+    G = rng.standard_normal((3, 40, 24)).astype(np.float32)
+    v = rng.standard_normal((2, 3, 40, 24)).astype(np.float32)
+    out, vv = O.bank_step(G, v, 0.95, 0.85, 0.4385)
+    one, v1 = O.bank_step(G[1:2], v[:, 1:2], 0.95, 0.85, 0.4385)
+    assert np.array_equal(out[1:2], one)
+    assert np.array_equal(vv[:, 1:2], v1)
+
+
+def test_split_rule_is_by_rows():
+    """Split iff rows > 1024, for either orientation."""
+    rng = np.random.default_rng(15)
+    X = O.R(rng.standard_normal((1, 1032, 16)).astype(np.float32))
+    assert np.array_equal(O.cascade(X), O.cascade(X, split=True))
+    Xw = O.R(rng.standard_normal((1, 16, 1032)).astype(np.float32))
+    assert np.array_equal(O.cascade(Xw), O.cascade(Xw, split=False))
+
+
+def test_map0_reuses_rescaled_gram_golden():
+    c = json.load(open(GOLDEN))["map0_uses_rescaled_gram"]
+    X = np.array(c["X"], np.float32)[None]
+    out = O.cascade(X, maps=[tuple(m) for m in c["maps"]])
+    assert np.array_equal(out[0], np.array(c["out"], np.float32))
+
+
+def test_zero_padding_invariance_fixes_orientation():
+    """Zero rows or columns add exact zeros to every product, so a zero column turns a square (or
+    wide) X into a wide matrix with the same result, and a zero row turns a tall X into a taller one
+    with the same result.  Square matrices therefore follow the wide branch."""
+    rng = np.random.default_rng(16)
+    for m, n in [(24, 24), (16, 40), (40, 16)]:
+        X = O.R(rng.standard_normal((2, m, n)).astype(np.float32))
+        base = O.cascade(X)
+        if m <= n:
+            padded = np.concatenate([X, np.zeros((2, m, 1), np.float32)], axis=2)
+            assert np.array_equal(O.cascade(padded)[:, :, :n], base), (m, n)
+        if m > n:
+            padded = np.concatenate([X, np.zeros((2, 1, n), np.float32)], axis=1)
+            assert np.array_equal(O.cascade(padded)[:, :m, :], base), (m, n)
+    # the square case does differ between the branches in bf16, so the check above has teeth
+    X = O.R(rng.standard_normal((1, 24, 24)).astype(np.float32))
+    tall_route = np.swapaxes(O.cascade(np.swapaxes(X, 1, 2).copy()), 1, 2)
+    assert not np.array_equal(tall_route, O.cascade(X))
