@@ -1,0 +1,225 @@
+"""Benchmark of the ANVIL bank step on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload mlp|qk|vo|vs|us|single_wide] [--all]
+                    [--no-cpu-baseline] [--stages]
+
+A step is one anvil_bank_step call over the whole stack (momentum, normalisation and the six
+Gram / polynomial / apply maps) on a gradient already resident in HBM.  The default workload is
+the 24 x 2816 x 768 mlp bank.  One JSON line goes to stdout; --all adds one line per workload
+(to stderr, so the first stdout line stays the contract line).
+
+Roofline: the dominant kernel is the apply GEMM (61% of the cascade's flops on the mlp bank).  Its
+average launch duration is measured here with HIP events around a loop of apply launches on the
+same stream and shapes; `achieved` = algorithmic flops of one launch / that duration.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "ANVIL bank-step matrices/s + TFLOP/s (% bf16 MFMA peak), 24×2816×768 mlp bank"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+
+
+def flops(g, m, n):
+    """Algorithmic flops of one bank step (symmetric halves of A and B not counted).
+
+    Per matrix and map: Gram s(s+1)L, polynomial s^2(s+1), apply 2 s^2 L; six maps."""
+    s, L = min(m, n), max(m, n)
+    gram = s * (s + 1) * L
+    poly = s * s * (s + 1)
+    apply = 2 * s * s * L
+    return {"gram": 6 * g * gram, "poly": 6 * g * poly, "apply": 6 * g * apply,
+            "total": 6 * g * (gram + poly + apply)}
+
+
+def momentum_bytes(g, m, n):
+    return 22 * g * m * n
+
+
+def _events():
+    import torch
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def time_bank_step(anvil, w, steps, warmup):
+    import torch
+    g, m, n = w.g, w.m, w.n
+    dev = torch.device("cuda:0")
+    G = torch.from_numpy(w.grad(w.measured[0])).to(dev)
+    vel = torch.zeros((2, g, m, n), dtype=torch.float32, device=dev)
+    out = torch.empty((g, m, n), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(anvil.workspace_bytes(g, m, n), dtype=torch.uint8, device=dev)
+    mu, fb, fw = anvil.rail_scalars(w.step_ids[w.measured[0]])
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        anvil.anvil_bank_step(G, vel, mu, fb, fw, out=out, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = _events()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        anvil.anvil_bank_step(G, vel, mu, fb, fw, out=out, workspace=ws, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / steps
+    return ms, wall, (G, vel, out)
+
+
+def time_stages(anvil, w, reps=20):
+    """Average duration of each stage kernel (HIP events around `reps` launches on one stream)."""
+    import torch
+    g, m, n = w.g, w.m, w.n
+    s = min(m, n)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    G = torch.from_numpy(w.grad(w.measured[0])).to(dev)
+    vel = torch.zeros((2, g, m, n), dtype=torch.float32, device=dev)
+    x = anvil.anvil_momentum(G, vel, 0.95, 0.85, 1.0)
+    a, parts = anvil.anvil_gram(x, want_trace=True)
+    anvil.anvil_normalize(x, a, parts)
+    b = anvil.anvil_poly(a, -6.095026865488, 3.905234618423)
+    c = torch.empty_like(x)
+    xs = torch.empty_like(x)
+    split = m > 1024
+    res = {}
+
+    def timed(name, fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = _events()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / reps * 1e3   # microseconds per launch
+
+    timed("momentum", lambda: anvil.anvil_momentum(G, vel, 0.95, 0.85, 1.0, x_out=xs, stream=stream))
+    timed("gram", lambda: anvil.anvil_gram(x, a_out=a, stream=stream))
+    timed("poly", lambda: anvil.anvil_poly(a, -3.3, 0.99, b_out=b, stream=stream))
+    timed("apply", lambda: anvil.anvil_apply(x, b, 3.2, split, c_out=c, stream=stream))
+    return res
+
+
+def cpu_baseline(w, budget_s=20.0):
+    """The oracle on a bounded sample of the same workload: whole bank steps of single matrices
+    until about budget_s of CPU time, reported as matrices/s."""
+    from oracle import anvil_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        threads = os.cpu_count()
+    G = w.grad(w.measured[0], g=1)
+    v = np.zeros((2,) + G.shape, np.float32)
+    mu, fb, fw = 0.95, 0.85, 1.0
+    done, t0 = 0, time.perf_counter()
+    while True:
+        O.bank_step(G, v, mu, fb, fw)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or done >= 8:
+            break
+    return {"value": done / el, "unit": "matrices/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} single-matrix bank steps ({w.m}x{w.n}, numpy fp64 products with "
+                      f"bf16 rounding emulation), {el:.1f} s"}
+
+
+def run_workload(anvil, name, steps, warmup, with_stages=True):
+    from orthogonalizing_polynomial_cascade_amd import workloads
+    w = workloads.ALL[name]()
+    ms, wall, _ = time_bank_step(anvil, w, steps, warmup)
+    f = flops(w.g, w.m, w.n)
+    rec = {
+        "workload": name, "g": w.g, "m": w.m, "n": w.n,
+        "ms_per_step": ms, "matrices_per_s": w.g / (ms * 1e-3),
+        "tflops": f["total"] / (ms * 1e-3) / 1e12,
+        "wall_s": wall,
+    }
+    rec["pct_bf16_peak"] = 100.0 * rec["tflops"] / PEAK_BF16_TFLOPS
+    if with_stages:
+        st = time_stages(anvil, w)
+        rec["stage_us"] = st
+        rec["momentum_gbs"] = momentum_bytes(w.g, w.m, w.n) / (st["momentum"] * 1e-6) / 1e9
+        for k in ("gram", "poly", "apply"):
+            rec[f"{k}_tflops"] = f[k] / 6 / (st[k] * 1e-6) / 1e12
+    return w, rec
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mlp")
+    ap.add_argument("--all", action="store_true", help="also report every workload (stderr)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the ANVIL bank step has no cross-GPU path in this build "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from orthogonalizing_polynomial_cascade_amd import anvil
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    anvil.load()
+
+    w, rec = run_workload(anvil, args.workload, args.steps, args.warmup)
+    f = flops(w.g, w.m, w.n)
+    apply_us = rec["stage_us"]["apply"]
+    apply_flops = f["apply"] / 6
+    achieved = apply_flops / (apply_us * 1e-6) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": rec["matrices_per_s"],
+        "unit": "matrices/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": rec["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name} bank {w.g}x{w.m}x{w.n} (fp32 grads, fp32 rails, "
+                               f"bf16 cascade, 6 maps)", "g": w.g, "m": w.m, "n": w.n,
+                   "parallelism": "single GPU"},
+        "tflops": rec["tflops"],
+        "pct_bf16_peak": rec["pct_bf16_peak"],
+        "stage_us": rec["stage_us"],
+        "momentum_gbs": rec["momentum_gbs"],
+        "momentum_pct_hbm": 100.0 * rec["momentum_gbs"] / PEAK_HBM_GBS,
+        "gram_tflops": rec["gram_tflops"],
+        "poly_tflops": rec["poly_tflops"],
+        "apply_tflops": rec["apply_tflops"],
+        "roofline": {"bound": "mfma", "kernel": "apply (gemm_kernel<2>)", "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+    if args.all:
+        for name in ("single_wide", "qk", "vo", "mlp", "vs", "us"):
+            _, r = run_workload(anvil, name, max(10, args.steps // 2), args.warmup)
+            print(json.dumps(r), file=sys.stderr, flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -26,6 +26,9 @@ Precision model (the plainest reading of the page; each point is listed in DESIG
     form, a bmm into a bf16 buffer followed by an in-place add of a*X).
 
 `exact=True` replaces every rounding by the identity and runs in fp64; the spectral tests use it.
+`acc="fp32"` accumulates the products in fp32 (library sgemm order) instead of fp64: a second,
+equally valid accumulation order, used to measure the rounding-noise floor of an input (how far two
+correct implementations of the same rounding points drift apart on it).
 
 Pins (tests/test_oracle_*.py): bf16 rounding against torch's CPU cast over edge bit patterns;
 the rails against the closed form of a constant-gradient EMA; the Gram against exact rational
@@ -144,8 +147,15 @@ def momentum_step(grad, velocity, momentum, fast_beta, fast_weight):
 # Step 3-4: Gram, trace normalisation, the quintic maps
 # --------------------------------------------------------------------------------------------
 
-def _mm(p, q):
-    """fp64 product of two operands (bf16 values held in fp32, or fp64 in exact mode)."""
+def _mm(p, q, acc: str = "fp64"):
+    """Product of two operands (bf16 values held in fp32, or fp64 in exact mode).
+
+    acc="fp64": accumulated in fp64 (the default, the closest to the exact product).
+    acc="fp32": accumulated in fp32 by the BLAS sgemm -- another valid accumulation order, used
+    only to measure how far two correct implementations drift apart on a given input.
+    """
+    if acc == "fp32":
+        return np.matmul(np.asarray(p, dtype=F32), np.asarray(q, dtype=F32))
     return np.matmul(np.asarray(p, dtype=np.float64), np.asarray(q, dtype=np.float64))
 
 
@@ -153,9 +163,9 @@ def _swapT(x):
     return np.swapaxes(x, -1, -2)
 
 
-def gram(X, tall: bool, exact: bool = False):
+def gram(X, tall: bool, exact: bool = False, acc: str = "fp64"):
     """A = X^T X (tall) or X X^T (wide); fp32 accumulation result rounded to bf16."""
-    P = _mm(_swapT(X), X) if tall else _mm(X, _swapT(X))
+    P = _mm(_swapT(X), X, acc) if tall else _mm(X, _swapT(X), acc)
     if exact:
         return P
     return R(P.astype(F32))
@@ -188,21 +198,21 @@ def normalize(X, A, d, exact: bool = False):
     return R(X.astype(F32) / d), R(A.astype(F32) / (d * d))
 
 
-def poly(A, b, c, exact: bool = False):
+def poly(A, b, c, exact: bool = False, acc: str = "fp64"):
     """B = b*A + c*(A @ A); the product is fp32 and the sum is formed in fp32 before rounding."""
     if exact:
         return b * A + c * _mm(A, A)
-    Q = _mm(A, A).astype(F32)
+    Q = _mm(A, A, acc).astype(F32)
     return R(F32(b) * A + F32(c) * Q)
 
 
-def apply(X, B, a, tall: bool, split: bool, exact: bool = False):
+def apply(X, B, a, tall: bool, split: bool, exact: bool = False, acc: str = "fp64"):
     """C = a*X + X@B (tall) or a*X + B@X (wide).
 
     Fused form: the fp32 product plus a*X, rounded once.  Split form (banks with more than 1024
     rows): the product is stored as bf16 first, and a*X is added to that bf16 value in fp32.
     """
-    P = _mm(X, B) if tall else _mm(B, X)
+    P = _mm(X, B, acc) if tall else _mm(B, X, acc)
     if exact:
         return a * X + P
     P = P.astype(F32)
@@ -213,7 +223,7 @@ def apply(X, B, a, tall: bool, split: bool, exact: bool = False):
 
 
 def cascade(X, split: bool | None = None, exact: bool = False, maps=ANVIL_MAPS,
-            return_trace: bool = False):
+            return_trace: bool = False, acc: str = "fp64"):
     """The orthogonalising cascade on a bf16 stack X [g, m, n] (values held as fp32).
 
     `split` defaults to the page's rule (more than 1024 rows).  Orientation: tall iff rows > cols,
@@ -225,14 +235,14 @@ def cascade(X, split: bool | None = None, exact: bool = False, maps=ANVIL_MAPS,
     tall = m > n
     if split is None:
         split = m > SPLIT_BADDBMM_MIN_ROWS
-    A = gram(X, tall, exact)
+    A = gram(X, tall, exact, acc)
     tr, d = trace_scale(A, exact)
     X, A = normalize(X, A, d, exact)
     for k, (a, b, c) in enumerate(maps):
         if k > 0:
-            A = gram(X, tall, exact)
-        B = poly(A, b, c, exact)
-        X = apply(X, B, a, tall, split, exact)
+            A = gram(X, tall, exact, acc)
+        B = poly(A, b, c, exact, acc)
+        X = apply(X, B, a, tall, split, exact, acc)
     if return_trace:
         return X, tr, d
     return X

@@ -1,0 +1,338 @@
+// C ABI of libanvil.so: argument checks, workspace management and the launch sequence of one
+// ANVIL bank step (modded-nanogpt anvil.py, `anvil_cascade`).
+#include <hip/hip_runtime.h>
+
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "../../include/anvil.h"
+#include "launchers.h"
+
+namespace {
+
+using anvil::Shape;
+
+// The six quintic maps (a, b, c) in application order (anvil.py, the table of maps), taken as
+// fp32 kernel arguments.
+const double kMaps[6][3] = {
+    {3.923798038567, -6.095026865488, 3.905234618423},
+    {3.278126713798, -3.328923386476, 0.989127286973},
+    {3.505298394150, -5.137358782410, 1.968325560615},
+    {2.815058591845, -3.685181239622, 1.417196497642},
+    {2.245503932403, -2.443826979899, 0.963091710461},
+    {2.256537145403, -2.166840097229, 0.929501253245},
+};
+
+// Banks with more rows than this use the split (two-rounding) apply (anvil.py).
+constexpr int64_t kSplitMinRows = 1024;
+
+thread_local int t_last_hip = 0;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return ANVIL_OK;
+  t_last_hip = static_cast<int>(e);
+  return ANVIL_ERR_HIP;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return na && nb && x < y + nb && y < x + na;
+}
+
+// Shape checks shared by every entry point.  Returns ANVIL_OK with *empty set for a zero-size
+// stack.
+int check_shape(int64_t g, int64_t m, int64_t n, Shape* sh, bool* empty) {
+  if (g < 0 || m < 0 || n < 0) return ANVIL_ERR_INVALID_ARG;
+  *empty = (g == 0 || m == 0 || n == 0);
+  if (*empty) return ANVIL_OK;
+  if (m % 8 != 0 || n % 8 != 0) return ANVIL_ERR_UNSUPPORTED;
+  if (g > 65535) return ANVIL_ERR_UNSUPPORTED;
+  if (m * n >= (int64_t(1) << 31)) return ANVIL_ERR_UNSUPPORTED;
+  sh->g = g;
+  sh->m = static_cast<int>(m);
+  sh->n = static_cast<int>(n);
+  return ANVIL_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Workspace regions: ping-pong X (bf16 [g,m,n]), A and B (bf16 [g,s,s]), trace partials
+// (fp32 [g, slots]) and d (fp32 [g]).
+struct Layout {
+  size_t ping, a, b, partials, d, total;
+};
+
+Layout layout_for(const Shape& sh) {
+  const size_t g = static_cast<size_t>(sh.g);
+  const size_t s = static_cast<size_t>(sh.s());
+  Layout l;
+  size_t off = 0;
+  l.ping = off;
+  off += round_up(g * sh.m * sh.n * 2);
+  l.a = off;
+  off += round_up(g * s * s * 2);
+  l.b = off;
+  off += round_up(g * s * s * 2);
+  l.partials = off;
+  off += round_up(g * anvil::gram_trace_slots(sh.s()) * 4);
+  l.d = off;
+  off += round_up(g * 4);
+  l.total = off;
+  return l;
+}
+
+int check_step_args(const float* grad, float* velocity, uint16_t* out, const Shape& sh) {
+  if (!grad || !velocity || !out) return ANVIL_ERR_INVALID_ARG;
+  if (!aligned(grad, 16) || !aligned(velocity, 16) || !aligned(out, 16)) return ANVIL_ERR_MISALIGNED;
+  const size_t cnt = static_cast<size_t>(sh.g) * sh.m * sh.n;
+  if (overlap(out, cnt * 2, grad, cnt * 4) || overlap(out, cnt * 2, velocity, cnt * 8) ||
+      overlap(grad, cnt * 4, velocity, cnt * 8))
+    return ANVIL_ERR_ALIAS;
+  return ANVIL_OK;
+}
+
+// The launch sequence: momentum, Gram 0 with trace, normalise, then six (Gram, poly, apply).
+// X starts in `out`; the apply ping-pongs between `out` and the workspace copy, and after the
+// sixth (an even number of) swaps the result is back in `out`.
+int run_step(const float* grad, float* velocity, float momentum, float fast_beta,
+             float fast_weight, uint16_t* out, const Shape& sh, char* ws, hipStream_t stream) {
+  const Layout l = layout_for(sh);
+  uint16_t* ping = reinterpret_cast<uint16_t*>(ws + l.ping);
+  uint16_t* A = reinterpret_cast<uint16_t*>(ws + l.a);
+  uint16_t* B = reinterpret_cast<uint16_t*>(ws + l.b);
+  float* partials = reinterpret_cast<float*>(ws + l.partials);
+  float* d = reinterpret_cast<float*>(ws + l.d);
+  const int64_t count = sh.g * sh.m * sh.n;
+  const bool split = sh.m > kSplitMinRows;
+
+  hipError_t e = anvil::launch_momentum(grad, velocity, velocity + count, out, count, momentum,
+                                        fast_beta, fast_weight, stream);
+  if (e != hipSuccess) return hip_status(e);
+  uint16_t* X = out;
+  uint16_t* Y = ping;
+  e = anvil::launch_gram(X, A, partials, sh, stream);
+  if (e != hipSuccess) return hip_status(e);
+  e = anvil::launch_normalize(X, A, partials, d, sh, stream);
+  if (e != hipSuccess) return hip_status(e);
+  for (int k = 0; k < 6; ++k) {
+    if (k > 0) {
+      e = anvil::launch_gram(X, A, nullptr, sh, stream);
+      if (e != hipSuccess) return hip_status(e);
+    }
+    e = anvil::launch_poly(A, B, static_cast<float>(kMaps[k][1]), static_cast<float>(kMaps[k][2]),
+                           sh.g, sh.s(), stream);
+    if (e != hipSuccess) return hip_status(e);
+    e = anvil::launch_apply(X, B, Y, static_cast<float>(kMaps[k][0]), split, sh, stream);
+    if (e != hipSuccess) return hip_status(e);
+    std::swap(X, Y);
+  }
+  return ANVIL_OK;
+}
+
+// Workspace cache of the allocating entry point, one grow-only buffer per (device, stream).
+std::mutex g_ws_mutex;
+std::map<std::pair<int, hipStream_t>, std::pair<void*, size_t>> g_ws;
+
+}  // namespace
+
+extern "C" {
+
+const char* anvil_status_string(int status) {
+  switch (status) {
+    case ANVIL_OK: return "ok";
+    case ANVIL_ERR_INVALID_ARG: return "invalid argument (null pointer, negative size or bad flag)";
+    case ANVIL_ERR_UNSUPPORTED:
+      return "unsupported shape (m and n must be multiples of 8, m*n < 2^31, g <= 65535) or workspace too small";
+    case ANVIL_ERR_MISALIGNED: return "pointer not 16-byte aligned (workspace: 256-byte)";
+    case ANVIL_ERR_ALIAS: return "an output overlaps an input";
+    case ANVIL_ERR_OOM: return "workspace allocation failed";
+    case ANVIL_ERR_HIP: return "HIP runtime or launch error (see anvil_last_hip_error)";
+    default: return "unknown status";
+  }
+}
+
+int anvil_last_hip_error(void) { return t_last_hip; }
+
+int anvil_version(void) { return 100; }
+
+size_t anvil_workspace_bytes(int64_t g, int64_t m, int64_t n) {
+  Shape sh;
+  bool empty = false;
+  if (check_shape(g, m, n, &sh, &empty) != ANVIL_OK || empty) return 0;
+  return layout_for(sh).total;
+}
+
+int anvil_bank_step_ws(const float* grad, float* velocity, float momentum, float fast_beta,
+                       float fast_weight, uint16_t* out, int64_t g, int64_t m, int64_t n,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  Shape sh;
+  bool empty = false;
+  int st = check_shape(g, m, n, &sh, &empty);
+  if (st != ANVIL_OK || empty) return st;
+  st = check_step_args(grad, velocity, out, sh);
+  if (st != ANVIL_OK) return st;
+  if (!workspace) return ANVIL_ERR_INVALID_ARG;
+  if (!aligned(workspace, kAlign)) return ANVIL_ERR_MISALIGNED;
+  const Layout l = layout_for(sh);
+  if (workspace_bytes < l.total) return ANVIL_ERR_UNSUPPORTED;
+  const size_t cnt = static_cast<size_t>(sh.g) * sh.m * sh.n;
+  if (overlap(workspace, l.total, grad, cnt * 4) || overlap(workspace, l.total, velocity, cnt * 8) ||
+      overlap(workspace, l.total, out, cnt * 2))
+    return ANVIL_ERR_ALIAS;
+  return run_step(grad, velocity, momentum, fast_beta, fast_weight, out, sh,
+                  static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+}
+
+int anvil_bank_step(const float* grad, float* velocity, float momentum, float fast_beta,
+                    float fast_weight, uint16_t* out, int64_t g, int64_t m, int64_t n,
+                    void* stream) {
+  Shape sh;
+  bool empty = false;
+  int st = check_shape(g, m, n, &sh, &empty);
+  if (st != ANVIL_OK || empty) return st;
+  st = check_step_args(grad, velocity, out, sh);
+  if (st != ANVIL_OK) return st;
+  const size_t need = layout_for(sh).total;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  void* ws = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    auto& slot = g_ws[{dev, hs}];
+    if (slot.second < need) {
+      if (slot.first) {
+        // the old buffer may still be in use by work queued on this stream
+        e = hipStreamSynchronize(hs);
+        if (e != hipSuccess) return hip_status(e);
+        e = hipFree(slot.first);
+        slot = {nullptr, 0};
+        if (e != hipSuccess) return hip_status(e);
+      }
+      void* p = nullptr;
+      if (hipMalloc(&p, need) != hipSuccess || !p) {
+        (void)hipGetLastError();
+        return ANVIL_ERR_OOM;
+      }
+      slot = {p, need};
+    }
+    ws = slot.first;
+  }
+  return run_step(grad, velocity, momentum, fast_beta, fast_weight, out, sh,
+                  static_cast<char*>(ws), hs);
+}
+
+int anvil_release_workspaces(void) {
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  int st = ANVIL_OK;
+  int cur = 0;
+  const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+  for (auto& kv : g_ws) {
+    if (!kv.second.first) continue;
+    hipError_t e = hipSetDevice(kv.first.first);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e == hipSuccess) e = hipFree(kv.second.first);
+    if (e != hipSuccess) st = hip_status(e);
+  }
+  g_ws.clear();
+  if (have_cur) (void)hipSetDevice(cur);
+  return st;
+}
+
+int anvil_momentum(const float* grad, float* velocity, float momentum, float fast_beta,
+                   float fast_weight, uint16_t* x_out, int64_t g, int64_t m, int64_t n,
+                   void* stream) {
+  Shape sh;
+  bool empty = false;
+  int st = check_shape(g, m, n, &sh, &empty);
+  if (st != ANVIL_OK || empty) return st;
+  st = check_step_args(grad, velocity, x_out, sh);
+  if (st != ANVIL_OK) return st;
+  const int64_t count = sh.g * sh.m * sh.n;
+  return hip_status(anvil::launch_momentum(grad, velocity, velocity + count, x_out, count,
+                                           momentum, fast_beta, fast_weight,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int64_t anvil_trace_slots(int64_t m, int64_t n) {
+  Shape sh;
+  bool empty = false;
+  if (check_shape(1, m, n, &sh, &empty) != ANVIL_OK || empty) return 0;
+  return anvil::gram_trace_slots(sh.s());
+}
+
+int anvil_gram(const uint16_t* x, uint16_t* a_out, float* trace_partials, int64_t g, int64_t m,
+               int64_t n, void* stream) {
+  Shape sh;
+  bool empty = false;
+  int st = check_shape(g, m, n, &sh, &empty);
+  if (st != ANVIL_OK || empty) return st;
+  if (!x || !a_out) return ANVIL_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(a_out, 16) || (trace_partials && !aligned(trace_partials, 16)))
+    return ANVIL_ERR_MISALIGNED;
+  const size_t s = sh.s();
+  const size_t xb = static_cast<size_t>(sh.g) * sh.m * sh.n * 2, ab = sh.g * s * s * 2;
+  const size_t tb = static_cast<size_t>(sh.g) * anvil::gram_trace_slots(sh.s()) * 4;
+  if (overlap(a_out, ab, x, xb) || (trace_partials && (overlap(trace_partials, tb, x, xb) ||
+                                                       overlap(trace_partials, tb, a_out, ab))))
+    return ANVIL_ERR_ALIAS;
+  return hip_status(anvil::launch_gram(x, a_out, trace_partials, sh,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int anvil_normalize(uint16_t* x, uint16_t* a, const float* trace_partials, float* d_out,
+                    int64_t g, int64_t m, int64_t n, void* stream) {
+  Shape sh;
+  bool empty = false;
+  int st = check_shape(g, m, n, &sh, &empty);
+  if (st != ANVIL_OK || empty) return st;
+  if (!x || !a || !trace_partials) return ANVIL_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(a, 16) || !aligned(trace_partials, 4) ||
+      (d_out && !aligned(d_out, 4)))
+    return ANVIL_ERR_MISALIGNED;
+  const size_t s = sh.s();
+  const size_t xb = static_cast<size_t>(sh.g) * sh.m * sh.n * 2, ab = sh.g * s * s * 2;
+  const size_t tb = static_cast<size_t>(sh.g) * anvil::gram_trace_slots(sh.s()) * 4;
+  if (overlap(x, xb, a, ab) || overlap(x, xb, trace_partials, tb) || overlap(a, ab, trace_partials, tb) ||
+      (d_out && (overlap(d_out, sh.g * 4, x, xb) || overlap(d_out, sh.g * 4, a, ab) ||
+                 overlap(d_out, sh.g * 4, trace_partials, tb))))
+    return ANVIL_ERR_ALIAS;
+  return hip_status(anvil::launch_normalize(x, a, trace_partials, d_out, sh,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int anvil_poly(const uint16_t* a, uint16_t* b_out, float coef_b, float coef_c, int64_t g,
+               int64_t s, void* stream) {
+  Shape sh;
+  bool empty = false;
+  int st = check_shape(g, s, s, &sh, &empty);
+  if (st != ANVIL_OK || empty) return st;
+  if (!a || !b_out) return ANVIL_ERR_INVALID_ARG;
+  if (!aligned(a, 16) || !aligned(b_out, 16)) return ANVIL_ERR_MISALIGNED;
+  const size_t bytes = static_cast<size_t>(sh.g) * s * s * 2;
+  if (overlap(a, bytes, b_out, bytes)) return ANVIL_ERR_ALIAS;
+  return hip_status(anvil::launch_poly(a, b_out, coef_b, coef_c, sh.g, sh.m,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int anvil_apply(const uint16_t* x, const uint16_t* b, uint16_t* c_out, float coef_a, int split,
+                int64_t g, int64_t m, int64_t n, void* stream) {
+  Shape sh;
+  bool empty = false;
+  int st = check_shape(g, m, n, &sh, &empty);
+  if (st != ANVIL_OK || empty) return st;
+  if (!x || !b || !c_out || (split != 0 && split != 1)) return ANVIL_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(b, 16) || !aligned(c_out, 16)) return ANVIL_ERR_MISALIGNED;
+  const size_t s = sh.s();
+  const size_t xb = static_cast<size_t>(sh.g) * sh.m * sh.n * 2, bb = sh.g * s * s * 2;
+  if (overlap(c_out, xb, x, xb) || overlap(c_out, xb, b, bb)) return ANVIL_ERR_ALIAS;
+  return hip_status(anvil::launch_apply(x, b, c_out, coef_a, split != 0, sh,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

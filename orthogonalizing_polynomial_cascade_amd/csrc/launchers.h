@@ -1,0 +1,35 @@
+// Host-side launchers of the ANVIL kernels (internal to libanvil.so).  Arguments are checked by
+// the C ABI layer before these are called; each returns the hipError_t of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace anvil {
+
+// Fused twin-rail momentum + bf16 cast over `count` elements (count % 8 == 0).
+hipError_t launch_momentum(const float* grad, float* v0, float* v1, uint16_t* x, int64_t count,
+                           float momentum, float fast_beta, float fast_weight, hipStream_t stream);
+
+// Geometry of one bank: stack g of m x n matrices.
+struct Shape {
+  int64_t g;
+  int m, n;
+  bool tall() const { return m > n; }
+  int s() const { return m > n ? n : m; }
+  int L() const { return m > n ? m : n; }
+};
+
+// Number of diagonal tiles of the Gram (trace partials per matrix).
+int gram_trace_slots(int s);
+
+hipError_t launch_gram(const uint16_t* x, uint16_t* a, float* trace_partials, const Shape& sh,
+                       hipStream_t stream);
+hipError_t launch_normalize(uint16_t* x, uint16_t* a, const float* trace_partials, float* d,
+                            const Shape& sh, hipStream_t stream);
+hipError_t launch_poly(const uint16_t* a, uint16_t* b, float coef_b, float coef_c, int64_t g,
+                       int s, hipStream_t stream);
+hipError_t launch_apply(const uint16_t* x, const uint16_t* b, uint16_t* c, float coef_a,
+                        bool split, const Shape& sh, hipStream_t stream);
+
+}  // namespace anvil

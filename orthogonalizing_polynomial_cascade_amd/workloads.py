@@ -24,8 +24,10 @@ import numpy as np
 F32 = np.float32
 
 
-def _rng(seed: int) -> np.random.Generator:
-    return np.random.Generator(np.random.PCG64(seed))
+def _rng(seed: int, index: int | None = None) -> np.random.Generator:
+    """PCG64 stream for a seed, or for (seed, matrix index) when each matrix of a stack draws its
+    own fixed part -- so any prefix of a stack is the same whatever its length."""
+    return np.random.Generator(np.random.PCG64(seed if index is None else [seed, index]))
 
 
 @dataclass
@@ -51,17 +53,20 @@ def _fixed(w: Workload, key, make):
 
 
 def _single_wide(w, t, g):
-    r = _rng(101 + 7919 * t)
-    z = r.standard_normal((g, w.m, w.n))
-    scale = np.exp(r.standard_normal((g, w.m, 1)))
-    return (z * scale).astype(F32)
+    out = np.empty((g, w.m, w.n), F32)
+    for i in range(g):
+        r = _rng(101 + 7919 * t, i)
+        z = r.standard_normal((w.m, w.n))
+        scale = np.exp(r.standard_normal((w.m, 1)))
+        out[i] = z * scale
+    return out
 
 
 def _qk(w, t, g):
     def spikes():
-        r = _rng(2999)
         us, vs = [], []
-        for _ in range(w.g):
+        for i in range(w.g):
+            r = _rng(2999, i)
             us.append(np.linalg.qr(r.standard_normal((w.m, 8)))[0])
             vs.append(np.linalg.qr(r.standard_normal((w.n, 8)))[0])
         return np.stack(us), np.stack(vs)
@@ -76,16 +81,20 @@ def _qk(w, t, g):
 
 
 def _vo(w, t, g):
-    cols = _fixed(w, "cols", lambda: np.exp(2.0 * _rng(3999).standard_normal((w.g, 1, w.n))))
+    cols = _fixed(w, "cols", lambda: np.stack(
+        [np.exp(2.0 * _rng(3999, i).standard_normal((1, w.n))) for i in range(w.g)]))
     z = _rng(3000 + t).standard_normal((g, w.m, w.n))
     return (z * cols[:g]).astype(F32)
 
 
 def _mlp(w, t, g):
     def lowrank():
-        r = _rng(4999)
-        P = r.standard_normal((w.g, w.m, 32))
-        Q = r.standard_normal((w.g, 32, w.n))
+        P = np.empty((w.g, w.m, 32))
+        Q = np.empty((w.g, 32, w.n))
+        for i in range(w.g):
+            r = _rng(4999, i)
+            P[i] = r.standard_normal((w.m, 32))
+            Q[i] = r.standard_normal((32, w.n))
         return P, Q
     P, Q = _fixed(w, "lowrank", lowrank)
     low = 10.0 * np.matmul(P[:g], Q[:g]) / np.sqrt(32.0)

@@ -1,0 +1,126 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol include/anvil.h declares,
+and rejects bad arguments before any HIP call (so these run without a GPU).  Fake, never
+dereferenced pointer values are used for the rejected calls."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from orthogonalizing_polynomial_cascade_amd import anvil
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "anvil.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(anvil_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return anvil.load()
+
+
+def test_every_declared_symbol_is_exported_and_bound(lib):
+    names = _declared()
+    assert len(names) >= 13
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(anvil.SIGNATURES), set(names) ^ set(anvil.SIGNATURES)
+
+
+def test_status_strings(lib):
+    for code in range(7):
+        s = lib.anvil_status_string(code)
+        assert s and len(s) > 1
+    assert lib.anvil_status_string(0) == b"ok"
+    assert b"unknown" in lib.anvil_status_string(99)
+    assert lib.anvil_version() >= 100
+    assert lib.anvil_last_hip_error() == 0
+
+
+A = 0x10000000      # fake, 256-byte aligned addresses far apart
+B = 0x20000000
+C = 0x30000000
+W = 0x40000000
+
+
+def _step(lib, grad=A, vel=B, out=C, g=2, m=64, n=32):
+    return lib.anvil_bank_step(grad, vel, 0.95, 0.85, 1.0, out, g, m, n, None)
+
+
+def _step_ws(lib, grad=A, vel=B, out=C, g=2, m=64, n=32, ws=W, wsb=1 << 30):
+    return lib.anvil_bank_step_ws(grad, vel, 0.95, 0.85, 1.0, out, g, m, n, ws, wsb, None)
+
+
+def test_empty_stack_is_a_noop(lib):
+    for g, m, n in [(0, 64, 32), (2, 0, 32), (2, 64, 0)]:
+        assert lib.anvil_bank_step(None, None, 0.95, 0.85, 1.0, None, g, m, n, None) == 0
+        assert lib.anvil_gram(None, None, None, g, m, n, None) == 0
+        assert lib.anvil_apply(None, None, None, 1.0, 0, g, m, n, None) == 0
+    assert lib.anvil_workspace_bytes(0, 64, 32) == 0
+
+
+def test_invalid_arguments(lib):
+    assert _step(lib, g=-1) == anvil.ANVIL_ERR_INVALID_ARG
+    assert _step(lib, m=-8) == anvil.ANVIL_ERR_INVALID_ARG
+    assert _step(lib, grad=None) == anvil.ANVIL_ERR_INVALID_ARG
+    assert _step(lib, vel=None) == anvil.ANVIL_ERR_INVALID_ARG
+    assert _step(lib, out=None) == anvil.ANVIL_ERR_INVALID_ARG
+    assert _step_ws(lib, ws=None) == anvil.ANVIL_ERR_INVALID_ARG
+    assert lib.anvil_apply(A, B, C, 1.0, 2, 1, 64, 32, None) == anvil.ANVIL_ERR_INVALID_ARG
+    assert lib.anvil_normalize(A, B, None, None, 1, 64, 32, None) == anvil.ANVIL_ERR_INVALID_ARG
+
+
+def test_unsupported_shapes(lib):
+    assert _step(lib, m=60) == anvil.ANVIL_ERR_UNSUPPORTED
+    assert _step(lib, n=30) == anvil.ANVIL_ERR_UNSUPPORTED
+    assert _step(lib, g=70000) == anvil.ANVIL_ERR_UNSUPPORTED
+    assert _step(lib, m=65536, n=32768) == anvil.ANVIL_ERR_UNSUPPORTED
+    assert lib.anvil_workspace_bytes(1, 60, 32) == 0
+    need = lib.anvil_workspace_bytes(2, 64, 32)
+    assert _step_ws(lib, wsb=need - 1) == anvil.ANVIL_ERR_UNSUPPORTED
+
+
+def test_misaligned(lib):
+    assert _step(lib, grad=A + 4) == anvil.ANVIL_ERR_MISALIGNED
+    assert _step(lib, vel=B + 8) == anvil.ANVIL_ERR_MISALIGNED
+    assert _step(lib, out=C + 2) == anvil.ANVIL_ERR_MISALIGNED
+    assert _step_ws(lib, ws=W + 16) == anvil.ANVIL_ERR_MISALIGNED
+
+
+def test_aliasing(lib):
+    assert _step(lib, out=A) == anvil.ANVIL_ERR_ALIAS
+    assert _step(lib, out=B + 64) == anvil.ANVIL_ERR_ALIAS
+    assert _step(lib, vel=A + 256) == anvil.ANVIL_ERR_ALIAS
+    assert _step_ws(lib, ws=C) == anvil.ANVIL_ERR_ALIAS
+    assert lib.anvil_apply(A, B, A, 1.0, 0, 1, 64, 32, None) == anvil.ANVIL_ERR_ALIAS
+    assert lib.anvil_apply(A, B, B, 1.0, 0, 1, 64, 32, None) == anvil.ANVIL_ERR_ALIAS
+    assert lib.anvil_poly(A, A, 1.0, 1.0, 1, 64, None) == anvil.ANVIL_ERR_ALIAS
+    assert lib.anvil_gram(A, A, None, 1, 64, 32, None) == anvil.ANVIL_ERR_ALIAS
+
+
+def test_workspace_size_and_trace_slots(lib):
+    g, m, n = 24, 2816, 768
+    ws = lib.anvil_workspace_bytes(g, m, n)
+    s = 768
+    assert ws >= g * m * n * 2 + 2 * g * s * s * 2 + g * 4
+    assert ws % 256 == 0
+    assert lib.anvil_trace_slots(2816, 768) >= 1
+    assert lib.anvil_trace_slots(256, 768) == lib.anvil_trace_slots(768, 256)
+    assert lib.anvil_trace_slots(7, 8) == 0
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    g = torch.zeros(1, 8, 8)
+    with pytest.raises(ValueError):
+        anvil.anvil_bank_step(g, torch.zeros(2, 1, 8, 8), 0.95, 0.85, 1.0)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError):
+        anvil.load(str(tmp_path / "libanvil.so"))

@@ -1,0 +1,220 @@
+"""Full bank-step parity (anvil_bank_step through the C ABI) against the oracle, plus the
+invariances that hold exactly on the GPU path.
+
+Bar: relative Frobenius error <= 1e-2 per matrix on the bf16 update, <= 1e-6 relative on the fp32
+rails, and on well-conditioned inputs every output singular value within 0.3 of 1.  Where the
+oracle's own fp64 and fp32-accumulation variants already differ by more than 1e-2 / 1.5 (inputs
+with most singular values far below the maps' window, e.g. the mlp bank after warm-up), the
+update bar is 1.5x that measured noise floor instead."""
+import numpy as np
+import pytest
+
+from oracle import anvil_oracle as O
+from orthogonalizing_polynomial_cascade_amd import workloads as W
+from tests.helpers import from_gpu, rel_fro, to_gpu_f32
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = 1e-2
+RAIL_TOL = 1e-6
+FLOOR_FACTOR = 1.5
+
+
+def _run_both(gpu_lib, grads, scalars, g, m, n, check_steps=None, matrices=None,
+              return_lookahead=False):
+    """Run a step sequence on the GPU (whole stack) and the oracle (selected matrices); compare the
+    rails every step and the update on check_steps.  Returns the last GPU update (numpy fp32)."""
+    import torch
+    matrices = list(range(g)) if matrices is None else matrices
+    vel = torch.zeros((2, g, m, n), dtype=torch.float32, device="cuda")
+    v_or = np.zeros((2, len(matrices), m, n), np.float32)
+    out = None
+    for t, (G, (mu, fb, fw)) in enumerate(zip(grads, scalars)):
+        out = gpu_lib.anvil_bank_step(to_gpu_f32(G), vel, mu, fb, fw)
+        v_or, y = O.momentum_step(G[matrices], v_or, mu, fb, fw)
+        v_gpu = from_gpu(vel)[:, matrices]
+        rail_err = np.max(np.abs(v_gpu - v_or) / np.maximum(np.abs(v_or), 1e-30))
+        assert rail_err <= RAIL_TOL, f"step {t}: rail relative error {rail_err:.2e}"
+        if check_steps is None or t in check_steps:
+            X = O.R(y)
+            want = O.cascade(X)
+            got = from_gpu(out)[matrices]
+            for i, mi in enumerate(matrices):
+                r = rel_fro(got[i], want[i])
+                if r > OUT_TOL:
+                    # the input may sit outside the maps' well-conditioned window, where bf16
+                    # rounding noise is amplified: then the bar is the drift between two correct
+                    # accumulation orders of the oracle itself (fp64 vs fp32 sgemm)
+                    floor = rel_fro(O.cascade(X[i:i + 1], acc="fp32")[0], want[i])
+                    tol = max(OUT_TOL, FLOOR_FACTOR * floor)
+                    assert r <= tol, (f"step {t} matrix {mi}: relative Frobenius {r:.3e} above "
+                                      f"{tol:.3e} (noise floor {floor:.3e})")
+    if return_lookahead:
+        return from_gpu(out), y
+    return from_gpu(out)
+
+
+def _gauss_steps(g, m, n, seed, steps):
+    w = W.gaussian(g, m, n, seed=seed, steps=range(steps))
+    return [w.grad(t) for t in range(steps)]
+
+
+CASES = [
+    ("wide_ragged", 3, 200, 328),
+    ("tall_ragged", 3, 392, 136),
+    ("square", 2, 264, 264),
+    ("tall_split", 2, 1096, 136),
+    ("wide_split", 2, 1040, 1064),
+    ("tiny", 2, 8, 16),
+    ("single_tile_edge", 1, 128, 136),
+]
+
+
+@pytest.mark.parametrize("name,g,m,n", CASES)
+def test_bank_step_parity(gpu_lib, name, g, m, n):
+    grads = _gauss_steps(g, m, n, seed=len(name), steps=3)
+    scalars = [(0.95, 0.85, 1.0), (0.95, 0.85, 1.0), (0.95, 0.85, 0.4385)]
+    out, y = _run_both(gpu_lib, grads, scalars, g, m, n, return_lookahead=True)
+    checked = 0
+    for i in range(g):
+        if _well_conditioned(y[i]):
+            sv = np.linalg.svd(out[i].astype(np.float64), compute_uv=False)
+            assert np.all(np.abs(sv - 1) <= 0.3), (name, i, sv.min(), sv.max())
+            checked += 1
+    if m != n and min(m, n) >= 64 and max(m, n) >= 1.5 * min(m, n):
+        assert checked == g, "clearly rectangular Gaussian stacks are well conditioned"
+
+
+def _well_conditioned(y):
+    """Every singular value of the normalised input inside the maps' convergence window
+    (sigma/d in [0.002, 1/1.05]), where the six maps land within 0.3 of 1."""
+    X = O.R(y).astype(np.float64)
+    sv = np.linalg.svd(X, compute_uv=False)
+    d = np.sqrt(np.sum(X * X)) * 1.05
+    return sv.min() / d >= 0.002
+
+
+@pytest.mark.parametrize("wname", ["single_wide", "qk", "vo", "mlp", "vs", "us"])
+def test_workload_distribution_small_stack(gpu_lib, wname):
+    """Each workload's value distribution at its real matrix shape, on a 2-matrix stack, over the
+    last two steps of its schedule (the mlp pair spans the engage step)."""
+    w = W.ALL[wname]()
+    g = min(2, w.g)
+    ids = w.step_ids[-2:] if len(w.step_ids) > 1 else w.step_ids
+    if wname == "mlp":
+        ids = [513, 514]
+    ts = [w.step_ids.index(s) for s in ids]
+    grads = [w.grad(t, g=g) for t in ts]
+    scalars = [gpu_lib.rail_scalars(s) for s in ids]
+    _run_both(gpu_lib, grads, scalars, g, w.m, w.n)
+
+
+def test_mlp_sequence_across_engage(gpu_lib):
+    """mlp bank distribution, 2 matrices, 20 warm-up steps and steps 490-539: rails every step,
+    the update at steps 490, 513, 514, 539."""
+    w = W.mlp_bank()
+    g = 2
+    grads = [w.grad(t, g=g) for t in range(len(w.step_ids))]
+    scalars = [gpu_lib.rail_scalars(s) for s in w.step_ids]
+    _run_both(gpu_lib, grads, scalars, g, w.m, w.n, check_steps=set(w.measured))
+
+
+@pytest.mark.parametrize("wname", ["single_wide", "qk", "vo", "mlp", "vs", "us"])
+def test_full_size_sampled(gpu_lib, wname):
+    """The full stack in the benchmark's launch configuration; the oracle checks sampled
+    matrices (first, second, last) on the last two steps of the schedule."""
+    w = W.ALL[wname]()
+    ids = w.step_ids[-2:] if len(w.step_ids) > 1 else w.step_ids
+    ts = [w.step_ids.index(s) for s in ids]
+    grads = [w.grad(t) for t in ts]
+    scalars = [gpu_lib.rail_scalars(s) for s in ids]
+    sample = sorted({0, min(1, w.g - 1), w.g - 1})
+    _run_both(gpu_lib, grads, scalars, w.g, w.m, w.n, check_steps={len(ids) - 1}, matrices=sample)
+
+
+def test_deterministic_and_batch_invariant(gpu_lib):
+    import torch
+    g, m, n = 4, 392, 136
+    G = to_gpu_f32(_gauss_steps(g, m, n, 5, 1)[0])
+    v0 = torch.randn((2, g, m, n), dtype=torch.float32, device="cuda")
+    v1 = v0.clone()
+    a = gpu_lib.anvil_bank_step(G, v0, 0.95, 0.85, 0.4385)
+    b = gpu_lib.anvil_bank_step(G, v1, 0.95, 0.85, 0.4385)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(v0, v1)
+    # batch invariance: the step of one matrix alone equals its slice of the stacked step
+    vs = torch.randn((2, g, m, n), dtype=torch.float32, device="cuda")
+    whole = gpu_lib.anvil_bank_step(G, vs.clone(), 0.95, 0.85, 0.4385)
+    for i in range(g):
+        one = gpu_lib.anvil_bank_step(G[i:i + 1].contiguous(), vs[:, i:i + 1].contiguous(), 0.95,
+                                      0.85, 0.4385)
+        assert torch.equal(one.view(torch.int16), whole[i:i + 1].view(torch.int16))
+
+
+def test_workspace_entry_and_streams_match(gpu_lib):
+    import torch
+    g, m, n = 2, 200, 328
+    G = to_gpu_f32(_gauss_steps(g, m, n, 9, 1)[0])
+    v = torch.randn((2, g, m, n), dtype=torch.float32, device="cuda")
+    ref = gpu_lib.anvil_bank_step(G, v.clone(), 0.95, 0.85, 1.0)
+    ws = torch.empty(gpu_lib.workspace_bytes(g, m, n), dtype=torch.uint8, device="cuda")
+    got = gpu_lib.anvil_bank_step(G, v.clone(), 0.95, 0.85, 1.0, workspace=ws)
+    assert torch.equal(ref.view(torch.int16), got.view(torch.int16))
+    s = torch.cuda.Stream()
+    v2 = v.clone()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        got2 = gpu_lib.anvil_bank_step(G, v2, 0.95, 0.85, 1.0)
+    s.synchronize()
+    assert torch.equal(ref.view(torch.int16), got2.view(torch.int16))
+
+
+def test_workspace_regrow_between_shapes(gpu_lib):
+    """The cached workspace grows for a larger shape and is reused for a smaller one."""
+    import torch
+    for (g, m, n) in [(1, 64, 32), (2, 392, 136), (1, 64, 32)]:
+        G = _gauss_steps(g, m, n, 3, 1)[0]
+        v = torch.zeros((2, g, m, n), dtype=torch.float32, device="cuda")
+        out = from_gpu(gpu_lib.anvil_bank_step(to_gpu_f32(G), v, 0.95, 0.85, 1.0))
+        _, y = O.momentum_step(G, np.zeros((2, g, m, n), np.float32), 0.95, 0.85, 1.0)
+        want = O.cascade(O.R(y))
+        for i in range(g):
+            assert rel_fro(out[i], want[i]) <= OUT_TOL
+    gpu_lib.release_workspaces()
+
+
+def test_zero_gradient_and_nan(gpu_lib):
+    import torch
+    g, m, n = 3, 72, 40
+    G = torch.zeros((g, m, n), dtype=torch.float32, device="cuda")
+    v = torch.zeros((2, g, m, n), dtype=torch.float32, device="cuda")
+    out = gpu_lib.anvil_bank_step(G, v, 0.95, 0.85, 1.0)
+    assert torch.all(out == 0)
+    G = torch.randn((g, m, n), dtype=torch.float32, device="cuda")
+    G[1, 5, 7] = float("nan")
+    v = torch.zeros((2, g, m, n), dtype=torch.float32, device="cuda")
+    out = gpu_lib.anvil_bank_step(G, v, 0.95, 0.85, 1.0).float()
+    assert torch.all(torch.isfinite(out[0])) and torch.all(torch.isfinite(out[2]))
+    assert torch.all(torch.isnan(out[1]))
+
+
+def test_empty_stack(gpu_lib):
+    import torch
+    G = torch.zeros((0, 64, 32), dtype=torch.float32, device="cuda")
+    v = torch.zeros((2, 0, 64, 32), dtype=torch.float32, device="cuda")
+    out = gpu_lib.anvil_bank_step(G, v, 0.95, 0.85, 1.0)
+    assert out.shape == (0, 64, 32)
+
+
+def test_transpose_symmetry_within_tolerance(gpu_lib):
+    """GPU(X^T) and GPU(X)^T follow different kernels (wide vs tall) but the same mathematics."""
+    import torch
+    g, m, n = 2, 392, 136
+    G = _gauss_steps(g, m, n, 21, 1)[0]
+    a = from_gpu(gpu_lib.anvil_bank_step(to_gpu_f32(G), torch.zeros((2, g, m, n), device="cuda"),
+                                         0.95, 0.85, 1.0))
+    Gt = np.ascontiguousarray(np.swapaxes(G, 1, 2))
+    b = from_gpu(gpu_lib.anvil_bank_step(to_gpu_f32(Gt), torch.zeros((2, g, n, m), device="cuda"),
+                                         0.95, 0.85, 1.0))
+    for i in range(g):
+        assert rel_fro(a[i], b[i].T) <= OUT_TOL
