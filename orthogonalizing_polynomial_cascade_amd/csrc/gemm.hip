@@ -7,32 +7,48 @@
 //
 // with a fused fp32 epilogue and a single bf16 rounding at the page's storage points:
 //
-//   Gram   A = X^T X (tall: P = Q = X read down its columns, "K-strided")
+//   Gram   A = X^T X (tall: P = Q = X read down its columns, "K-major")
 //          A = X X^T (wide: P = Q = X read along its rows, "K-contiguous")
 //          epilogue bf16(acc); optional trace partials of the bf16 diagonal.
 //   poly   B = b A + c A A   (A symmetric, so A A = A A^T: P = Q = A, K-contiguous)
 //          epilogue bf16(b * A[i][j] + c * acc).
-//   apply  tall: C = a X + X B   (P = X, Q = B rows; B symmetric so B[k][j] = B[j][k])
-//          wide: C = a X + B X   (P = B, Q(j, k) = X[k][j]: K-strided)
+//   apply  tall: C = a X + X B   (P = X, Q = rows of B; B symmetric so B[k][j] = B[j][k])
+//          wide: C = a X + B X   (P = B, Q(j, k) = X[k][j]: K-major)
 //          epilogue bf16(a * X[i][j] + acc), or with split rounding
 //          bf16(bf16(acc) + a * X[i][j]) (the page's two-kernel form for banks of > 1024 rows).
 //
-// The Gram and the polynomial are symmetric, so only tiles on or above the diagonal are computed;
-// each is stored twice (C[i][j] and C[j][i]) from the same fp32 value, which keeps the stored
-// matrices exactly symmetric.  Inside a diagonal tile only entries with i <= j are stored.
+// The Gram and the polynomial are symmetric: only tiles on or above the diagonal are computed,
+// and each is stored twice (C[i][j] and C[j][i]) from the same fp32 value, so the stored matrices
+// are exactly symmetric.  Inside a diagonal tile only entries with i <= j are stored directly.
 //
-// Tiling: 256 threads (4 waves of 64) per 128x128 output tile, waves in a 2x2 grid, each wave a
-// 64x64 block of 2x2 MFMA 32x32 fragments.  K advances in steps of 64 through double-buffered
-// LDS; the next K-slab is fetched into registers while the current one feeds the MFMAs, so one
-// barrier per slab suffices.  LDS rows hold one operand row with K contiguous (plus 8 bf16 of
-// padding), so each MFMA operand is one 16-byte LDS read per lane.  K-strided operands (X read
-// down its columns) are transposed on the way into LDS: a thread fetches a 4(k) x 8(i) block as
-// four 16-byte row segments and rewrites it as eight 4-element K-runs.
+// Pipeline (CDNA4 / gfx950):
+//  * Operand slabs (rows x 64 k) travel HBM -> LDS with buffer_load_dwordx4 ... lds (16 bytes per
+//    lane straight into LDS, no register staging) through a ring of STAGES LDS buffers; the loads
+//    for slab k+STAGES-1 are in flight while slab k feeds the MFMAs.  Lanes outside the matrix
+//    (ragged M, N or K edges) get an offset past the buffer's range, which loads zeros.
+//  * K-contiguous slabs are stored [row][64 k] with 16-byte slots XOR-swizzled by row, so that
+//    an MFMA operand (32 rows x 8 k) is one ds_read_b128 per lane without bank conflicts.
+//  * K-major slabs (X read down its columns) are stored [64 k][rows] as they arrive, slots
+//    swizzled by k; an MFMA operand is two ds_read_b64_tr_b16, the LDS transpose read: within a
+//    16-lane group, lanes 4j..4j+3 point at 16 consecutive rows of k-row j and lane r receives
+//    the 4 k-values of row r.  No VALU transposes.
+//  * Each wave owns a (BM/WM) x (BN/WN) block of 32x32 MFMA fragments.  Each 64-deep slab is
+//    accumulated into fresh registers and then added to the running sums with IEEE fp32 adds
+//    (the MFMA's own addition into a large running sum roughly doubles the drift from an fp64
+//    reference on low-rank-dominated inputs).
+//  * Tiles are ordered so that consecutive tiles of one matrix land on the same XCD (hardware
+//    dispatches workgroups round-robin over the 8 XCDs, each with its own L2).
+//  * The epilogue goes through LDS, 32 rows at a time per wave: rows leave as 16-byte stores, and
+//    the mirror of a symmetric tile is read down the LDS columns and also leaves as 16-byte
+//    stores.
 //
-// Shapes: M, N, K are multiples of 8; partial tiles at the M, N and K edges are zero-filled on
-// load and masked on store.
+// Shapes: M, N, K are multiples of 8 (16-byte rows).
 #include "device_common.h"
 #include "launchers.h"
+
+// m0 is written by the DMA inline assembly; the kernel has no other use of it (no indirect
+// register indexing), which is what the compiler's reserved-register warning is about.
+#pragma clang diagnostic ignored "-Winline-asm"
 
 namespace anvil {
 
@@ -40,18 +56,21 @@ namespace {
 
 enum { OP_GRAM = 0, OP_POLY = 1, OP_APPLY = 2 };
 
-constexpr int kThreads = 256;
-constexpr int kBM = 128;          // output tile rows
-constexpr int kBN = 128;          // output tile cols
-constexpr int kBK = 64;           // K per LDS slab
-constexpr int kPad = 8;           // bf16 padding per LDS row
-constexpr int kLds = kBK + kPad;  // LDS row pitch in bf16
+constexpr int kBK = 64;                  // K per slab
+constexpr uint32_t kOOB = 0x80000000u;   // buffer offset past any range: the load returns 0
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_ptr;
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
 struct GemmParams {
   const uint16_t* P;
   const uint16_t* Q;
   int64_t strideP, strideQ;   // elements between consecutive matrices of the stack
   int ldp, ldq;               // row pitch (elements) of the stored P and Q
+  uint32_t bytesP, bytesQ;    // bytes of one matrix of P and of Q (buffer range)
   int M, N, K;
   uint16_t* C;
   int64_t strideC;
@@ -63,103 +82,138 @@ struct GemmParams {
   float beta;                 // poly: c
   float* trace;               // Gram: per-matrix diagonal partials, or nullptr
   int trace_slots;
-  int tiles_m, tiles_n;
+  int tiles_m, tiles_n;       // tile grid of one matrix
+  int tiles;                  // tiles per matrix (upper triangle for Gram and poly)
+  int total;                  // tiles * g
   int split;
 };
 
-// Fetch one operand slab (R rows x kBK) from global memory into registers, then write it to LDS
-// as [row][k] with k contiguous.
-template <bool KSTRIDED, int R>
-struct SlabLoader;
+// ---------------------------------------------------------------------------------------------
+// LDS slab layouts
+// ---------------------------------------------------------------------------------------------
 
-// K-contiguous operand: element (row, k) at base[row * ld + k].  16-byte chunks of 8 k's.
-template <int R>
-struct SlabLoader<false, R> {
-  static constexpr int kChunksPerRow = kBK / 8;
-  static constexpr int kPerThread = R * kChunksPerRow / kThreads;
-  u32x4_t reg[kPerThread];
+// [ROWS][64] bf16: a row is 128 bytes = 8 slots of 16 bytes (8 k each).  Logical slot c of row r
+// sits at slot c ^ ((r >> 1) & 7): 16 consecutive rows read at one logical slot hit 16 distinct
+// 16-byte bank groups.
+template <int ROWS>
+struct KContig {
+  __device__ static __forceinline__ int offset(int row, int c) {
+    return row * 128 + ((c ^ ((row >> 1) & 7)) << 4);
+  }
+};
 
-  __device__ __forceinline__ void load(const uint16_t* base, int ld, int row0, int rows, int k0,
-                                       int K, int tid) {
+// [64][ROWS] bf16: a k-row is ROWS*2 bytes = ROWS/8 slots.  Logical slot c of k-row kr sits at
+// slot c ^ (4 * (kr & 3)).
+template <int ROWS>
+struct KMajor {
+  static_assert(ROWS >= 128, "K-major slabs need at least 16 slots per k-row");
+  __device__ static __forceinline__ int offset(int kr, int c) {
+    return kr * (ROWS * 2) + ((c ^ ((kr & 3) << 2)) << 4);
+  }
+};
+
+// Raw buffer resource (stride 0, flags word of the gfx9 family) over `bytes` bytes at `base`.
+// All four words are wave-uniform and live in SGPRs.
+__device__ __forceinline__ i32x4_t make_rsrc(const uint16_t* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a)));
+  r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a >> 32) & 0xFFFFu));
+  r[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+  r[3] = 0x00020000;
+  return r;
+}
+
+// 32-bit LDS address of a pointer into dynamic shared memory (wave-uniform).
+__device__ __forceinline__ uint32_t lds_addr(const char* ptr) {
+  return __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_ptr)(ptr))));
+}
+
+// One wave-instruction of DMA: lane L's 16 bytes at `voff` of the buffer land in LDS at
+// lds + 16*L.  Issued as inline assembly so that the compiler neither reorders it nor inserts its
+// own (conservative) waits on it; completion is tracked with wait_vmcnt below.
+__device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
+// Issue the DMA of one slab of an operand (rows row0.., k0..k0+63) into LDS at `dst`.  The slab
+// is ROWS/8 wave-instructions of 1 KB; instruction u lands at dst + u*1024, lane L's 16 bytes at
+// dst + u*1024 + 16*L.
+template <bool KMAJOR, int ROWS, int NW>
+__device__ __forceinline__ void issue_slab(i32x4_t rsrc, const char* dst, int ld,
+                                           int row0, int rows, int k0, int K, int wave,
+                                           int lane) {
+  static_assert((ROWS / 8) % NW == 0, "slab instructions must split evenly over the waves");
 #pragma unroll
-    for (int r = 0; r < kPerThread; ++r) {
-      const int c = tid + kThreads * r;
-      const int row = c / kChunksPerRow;
-      const int kc = c % kChunksPerRow;
+  for (int i = 0; i < ROWS / 8 / NW; ++i) {
+    const int u = wave + i * NW;
+    uint32_t voff;
+    if constexpr (!KMAJOR) {
+      const int row = 8 * u + (lane >> 3);
+      const int c = (lane & 7) ^ ((row >> 1) & 7);
       const int gr = row0 + row;
-      const int gk = k0 + kc * 8;
-      if (gr < rows && gk < K) {
-        reg[r] = *reinterpret_cast<const u32x4_t*>(base + (int64_t)gr * ld + gk);
-      } else {
-        reg[r] = u32x4_t{0u, 0u, 0u, 0u};
-      }
+      const int gk = k0 + c * 8;
+      voff = (gr < rows && gk < K) ? (uint32_t)(gr * ld + gk) * 2u : kOOB;
+    } else {
+      constexpr int kSlots = ROWS / 8;
+      constexpr int kRowsPerKb = 64 / kSlots;
+      const int kr = u * kRowsPerKb + lane / kSlots;
+      const int c = (lane % kSlots) ^ ((kr & 3) << 2);
+      const int gk = k0 + kr;
+      const int gr = row0 + c * 8;
+      voff = (gr < rows && gk < K) ? (uint32_t)(gk * ld + gr) * 2u : kOOB;
     }
+    dma16(rsrc, lds_addr(dst + u * 1024), voff);
   }
+}
 
-  __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
-#pragma unroll
-    for (int r = 0; r < kPerThread; ++r) {
-      const int c = tid + kThreads * r;
-      const int row = c / kChunksPerRow;
-      const int kc = c % kChunksPerRow;
-      *reinterpret_cast<u32x4_t*>(lds + row * kLds + kc * 8) = reg[r];
-    }
+// MFMA operand of a 32-row fragment (rows R0..R0+31) at k-step ks (k = 16ks .. 16ks+15):
+// lane l holds row R0 + l%32, k = 16ks + 8(l/32) + 0..7.
+template <bool KMAJOR, int ROWS>
+__device__ __forceinline__ bf16x8_t read_frag(const char* tile, int R0, int ks, int lane) {
+  if constexpr (!KMAJOR) {
+    const int row = R0 + (lane & 31);
+    const int c = 2 * ks + (lane >> 5);
+    return *reinterpret_cast<const bf16x8_t*>(tile + KContig<ROWS>::offset(row, c));
+  } else {
+    const int grp = lane >> 4;
+    const int r = lane & 15;
+    const int i = R0 + 16 * (grp & 1) + 4 * (r & 3);
+    const int kr = 16 * ks + 8 * (grp >> 1) + (r >> 2);
+    const int c = i >> 3;
+    const int half = ((i >> 2) & 1) * 8;
+    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4_ptr)(tile + KMajor<ROWS>::offset(kr, c) + half));
+    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4_ptr)(tile + KMajor<ROWS>::offset(kr + 4, c) + half));
+    const s16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8_t, v);
   }
-};
+}
 
-// K-strided operand: element (row, k) at base[k * ld + row].  A thread fetches 4 consecutive k
-// of 8 consecutive rows (four 16-byte segments) and transposes them in registers.
-template <int R>
-struct SlabLoader<true, R> {
-  static constexpr int kRowChunks = R / 8;
-  static constexpr int kBlocks = kRowChunks * (kBK / 4);
-  static constexpr int kPerThread = kBlocks / kThreads;
-  static_assert(kPerThread * kThreads == kBlocks, "slab must split evenly over the threads");
-  u32x4_t reg[kPerThread][4];
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
 
-  __device__ __forceinline__ void load(const uint16_t* base, int ld, int row0, int rows, int k0,
-                                       int K, int tid) {
-#pragma unroll
-    for (int r = 0; r < kPerThread; ++r) {
-      const int bidx = tid + kThreads * r;
-      const int ic = bidx % kRowChunks;
-      const int kq = bidx / kRowChunks;
-      const int gr = row0 + ic * 8;
-      const int gk = k0 + kq * 4;
-      const bool ok = gr < rows && gk < K;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        if (ok) {
-          reg[r][kk] = *reinterpret_cast<const u32x4_t*>(base + (int64_t)(gk + kk) * ld + gr);
-        } else {
-          reg[r][kk] = u32x4_t{0u, 0u, 0u, 0u};
-        }
-      }
-    }
-  }
+// Wait for this wave's LDS operations (lgkmcnt(0)).
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-  __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
-#pragma unroll
-    for (int r = 0; r < kPerThread; ++r) {
-      const int bidx = tid + kThreads * r;
-      const int ic = bidx % kRowChunks;
-      const int kq = bidx / kRowChunks;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        // dword j of each k-row holds rows 2j (low half) and 2j+1 (high half)
-        const uint32_t k0w = reg[r][0][j], k1w = reg[r][1][j];
-        const uint32_t k2w = reg[r][2][j], k3w = reg[r][3][j];
-        u32x2_t even, odd;
-        even[0] = (k0w & 0xFFFFu) | (k1w << 16);
-        even[1] = (k2w & 0xFFFFu) | (k3w << 16);
-        odd[0] = (k0w >> 16) | (k1w & 0xFFFF0000u);
-        odd[1] = (k2w >> 16) | (k3w & 0xFFFF0000u);
-        *reinterpret_cast<u32x2_t*>(lds + (ic * 8 + 2 * j) * kLds + kq * 4) = even;
-        *reinterpret_cast<u32x2_t*>(lds + (ic * 8 + 2 * j + 1) * kLds + kq * 4) = odd;
-      }
-    }
-  }
-};
+// Workgroup id -> logical tile id such that each XCD gets a contiguous run of logical ids.
+__device__ __forceinline__ int xcd_remap(int id, int total) {
+  constexpr int kXcd = 8;
+  const int q = total / kXcd;
+  const int r = total % kXcd;
+  const int x = id % kXcd;
+  const int local = id / kXcd;
+  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + local;
+}
 
 // Upper-triangle tile (ti <= tj) of linear index t, row by row.
 __device__ __forceinline__ void upper_tile(int t, int tiles, int* ti, int* tj) {
@@ -174,154 +228,267 @@ __device__ __forceinline__ void upper_tile(int t, int tiles, int* ti, int* tj) {
   *tj = i + t;
 }
 
-template <int OP, bool PT, bool QT>
-__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t sP[2][kBM * kLds];
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][kBN * kLds];
-  __shared__ float sRed[kThreads / 64];
+template <int BM, int BN, int WM, int WN, int STAGES>
+struct Cfg {
+  static constexpr int kWaves = WM * WN;
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int kWTM = BM / WM;   // wave tile rows
+  static constexpr int kWTN = BN / WN;   // wave tile cols
+  static constexpr int kFM = kWTM / 32;
+  static constexpr int kFN = kWTN / 32;
+  static constexpr int kStageBytes = (BM + BN) * 128;
+  static constexpr int kEpiPitch = kWTN + 4;                  // fp32 per LDS epilogue row
+  static constexpr int kEpiBytes = kWaves * 32 * kEpiPitch * 4;
+  static constexpr int kLdsBytes =
+      (STAGES * kStageBytes > kEpiBytes ? STAGES * kStageBytes : kEpiBytes);
+  static constexpr int kLoadsPerSlab = (BM / 8 + BN / 8) / kWaves;
+  static_assert(kWTM % 32 == 0 && kWTN % 32 == 0, "wave tile must be whole 32x32 fragments");
+  static_assert(kWTN % 8 == 0 && 64 % (kWTN / 8) == 0, "epilogue moves 8 columns per lane");
+  static_assert(STAGES >= 2, "at least double buffering");
+  static_assert(kLoadsPerSlab * (STAGES - 2) < 64, "vmcnt range");
+};
+
+template <int OP, bool PT, bool QT, int BM, int BN, int WM, int WN, int STAGES>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
+  using C = Cfg<BM, BN, WM, WN, STAGES>;
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  __shared__ float sRed[C::kWaves];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
-  const int64_t b = blockIdx.y;
+  const int wm = wave / WN;
+  const int wn = wave % WN;
 
+  const int logical = xcd_remap(blockIdx.x, p.total);
+  const int64_t b = logical / p.tiles;
+  const int t = logical % p.tiles;
   int ti, tj;
   if constexpr (OP == OP_APPLY) {
-    ti = blockIdx.x / p.tiles_n;
-    tj = blockIdx.x % p.tiles_n;
+    ti = t / p.tiles_n;
+    tj = t % p.tiles_n;
   } else {
-    upper_tile(blockIdx.x, p.tiles_m, &ti, &tj);
+    upper_tile(t, p.tiles_m, &ti, &tj);
   }
-  const int i0 = ti * kBM;
-  const int j0 = tj * kBN;
+  const int i0 = ti * BM;
+  const int j0 = tj * BN;
 
-  const uint16_t* Pb = p.P + b * p.strideP;
-  const uint16_t* Qb = p.Q + b * p.strideQ;
+  const i32x4_t rP = make_rsrc(p.P + b * p.strideP, p.bytesP);
+  const i32x4_t rQ = make_rsrc(p.Q + b * p.strideQ, p.bytesQ);
 
-  SlabLoader<PT, kBM> lp;
-  SlabLoader<QT, kBN> lq;
-
-  f32x16_t acc[2][2];
+  f32x16_t acc[C::kFM][C::kFN];
 #pragma unroll
-  for (int tm = 0; tm < 2; ++tm)
+  for (int fm = 0; fm < C::kFM; ++fm)
 #pragma unroll
-    for (int tn = 0; tn < 2; ++tn)
+    for (int fn = 0; fn < C::kFN; ++fn)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[tm][tn][r] = 0.0f;
+      for (int r = 0; r < 16; ++r) acc[fm][fn][r] = 0.0f;
 
   const int KT = (p.K + kBK - 1) / kBK;
-  lp.load(Pb, p.ldp, i0, p.M, 0, p.K, tid);
-  lq.load(Qb, p.ldq, j0, p.N, 0, p.K, tid);
-  lp.store(sP[0], tid);
-  lq.store(sQ[0], tid);
-  __syncthreads();
 
-  const int frag_row = lane & 31;
-  const int frag_k = (lane >> 5) * 8;
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < KT;
-    if (more) {
-      lp.load(Pb, p.ldp, i0, p.M, (kt + 1) * kBK, p.K, tid);
-      lq.load(Qb, p.ldq, j0, p.N, (kt + 1) * kBK, p.K, tid);
+  // prologue: slabs 0 .. STAGES-2 in flight
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s) {
+    if (s < KT) {
+      char* st = smem + s * C::kStageBytes;
+      issue_slab<PT, BM, C::kWaves>(rP, st, p.ldp, i0, p.M, s * kBK, p.K, wave, lane);
+      issue_slab<QT, BN, C::kWaves>(rQ, st + BM * 128, p.ldq, j0, p.N, s * kBK, p.K, wave, lane);
     }
-    const uint16_t* cp = sP[cur];
-    const uint16_t* cq = sQ[cur];
-    // Each slab accumulates into fresh registers and is then added to the running sums with IEEE
-    // fp32 adds: the MFMA's own addition into a large running accumulator is measurably less
-    // accurate (about twice the drift from an fp64 reference on low-rank-dominated inputs).
-    f32x16_t slab[2][2];
-#pragma unroll
-    for (int tm = 0; tm < 2; ++tm)
-#pragma unroll
-      for (int tn = 0; tn < 2; ++tn)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) slab[tm][tn][r] = 0.0f;
-#pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      bf16x8_t fa[2], fb[2];
-#pragma unroll
-      for (int tm = 0; tm < 2; ++tm)
-        fa[tm] = *reinterpret_cast<const bf16x8_t*>(
-            cp + (wm * 64 + tm * 32 + frag_row) * kLds + ks * 16 + frag_k);
-#pragma unroll
-      for (int tn = 0; tn < 2; ++tn)
-        fb[tn] = *reinterpret_cast<const bf16x8_t*>(
-            cq + (wn * 64 + tn * 32 + frag_row) * kLds + ks * 16 + frag_k);
-#pragma unroll
-      for (int tm = 0; tm < 2; ++tm)
-#pragma unroll
-        for (int tn = 0; tn < 2; ++tn)
-          slab[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[tm], fb[tn], slab[tm][tn], 0, 0, 0);
-    }
-#pragma unroll
-    for (int tm = 0; tm < 2; ++tm)
-#pragma unroll
-      for (int tn = 0; tn < 2; ++tn) acc[tm][tn] += slab[tm][tn];
-    if (more) {
-      lp.store(sP[cur ^ 1], tid);
-      lq.store(sQ[cur ^ 1], tid);
-    }
-    __syncthreads();
   }
 
-  // ---------------- epilogue ----------------
+  for (int kt = 0; kt < KT; ++kt) {
+    // slab kt has landed once at most STAGES-2 younger slabs of this wave are still in flight
+    if (KT - 1 - kt >= STAGES - 2) {
+      wait_vmcnt<C::kLoadsPerSlab * (STAGES - 2)>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __syncthreads();   // every wave's part of slab kt is in LDS; slab kt-1's buffer is free
+    {
+      const int kn = kt + STAGES - 1;
+      if (kn < KT) {
+        char* st = smem + (kn % STAGES) * C::kStageBytes;
+        issue_slab<PT, BM, C::kWaves>(rP, st, p.ldp, i0, p.M, kn * kBK, p.K, wave, lane);
+        issue_slab<QT, BN, C::kWaves>(rQ, st + BM * 128, p.ldq, j0, p.N, kn * kBK, p.K, wave,
+                                      lane);
+      }
+    }
+    const char* tp = smem + (kt % STAGES) * C::kStageBytes;
+    const char* tq = tp + BM * 128;
+
+    f32x16_t slab[C::kFM][C::kFN];
+#pragma unroll
+    for (int fm = 0; fm < C::kFM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < C::kFN; ++fn)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) slab[fm][fn][r] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      bf16x8_t fa[C::kFM], fb[C::kFN];
+#pragma unroll
+      for (int fm = 0; fm < C::kFM; ++fm)
+        fa[fm] = read_frag<PT, BM>(tp, wm * C::kWTM + fm * 32, ks, lane);
+#pragma unroll
+      for (int fn = 0; fn < C::kFN; ++fn)
+        fb[fn] = read_frag<QT, BN>(tq, wn * C::kWTN + fn * 32, ks, lane);
+#pragma unroll
+      for (int fm = 0; fm < C::kFM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < C::kFN; ++fn)
+          slab[fm][fn] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[fm], fb[fn], slab[fm][fn], 0, 0, 0);
+    }
+#pragma unroll
+    for (int fm = 0; fm < C::kFM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < C::kFN; ++fn) acc[fm][fn] += slab[fm][fn];
+  }
+  __syncthreads();   // every wave is done with the operand ring; reuse it for the epilogue
+
+  // ---------------- epilogue: per wave, 32 rows at a time through LDS ----------------
+  float* epi = reinterpret_cast<float*>(smem) + wave * 32 * C::kEpiPitch;
   uint16_t* Cb = p.C + b * p.strideC;
   const uint16_t* Eb = p.E ? p.E + b * p.strideE : nullptr;
+  const bool diag_tile = (OP != OP_APPLY) && ti == tj;
   float tsum = 0.0f;
+
 #pragma unroll
-  for (int tm = 0; tm < 2; ++tm) {
+  for (int fm = 0; fm < C::kFM; ++fm) {
+    // accumulators -> LDS (fp32): register r of lane l is row 8(r/4) + 4(l/32) + r%4, col l%32
 #pragma unroll
-    for (int tn = 0; tn < 2; ++tn) {
+    for (int fn = 0; fn < C::kFN; ++fn)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        // accumulator layout of the 32x32 MFMA: register r of lane l holds
-        // row 8*(r/4) + 4*(l/32) + r%4, column l%32
-        const int gi = i0 + wm * 64 + tm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int gj = j0 + wn * 64 + tn * 32 + (lane & 31);
-        if (gi >= p.M || gj >= p.N) continue;
-        const float v = acc[tm][tn][r];
-        if constexpr (OP == OP_APPLY) {
-          const float ax = p.alpha * bf16_to_f32(Eb[(int64_t)gi * p.lde + gj]);
-          uint32_t o;
+        const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int col = fn * 32 + (lane & 31);
+        epi[row * C::kEpiPitch + col] = acc[fm][fn][r];
+      }
+    wait_lds();
+    __builtin_amdgcn_wave_barrier();
+
+    const int gi0 = i0 + wm * C::kWTM + fm * 32;   // first global row of this block
+    const int gj0 = j0 + wn * C::kWTN;             // first global col of this wave
+
+    // direct rows: each lane takes 8 consecutive columns of one row
+    constexpr int kLanesPerRow = C::kWTN / 8;
+    constexpr int kRowsPerPass = 64 / kLanesPerRow;
+#pragma unroll
+    for (int pass = 0; pass < 32 / kRowsPerPass; ++pass) {
+      const int row = pass * kRowsPerPass + lane / kLanesPerRow;
+      const int col = (lane % kLanesPerRow) * 8;
+      const int gi = gi0 + row;
+      const int gj = gj0 + col;
+      if (gi >= p.M || gj >= p.N) continue;
+      const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(epi + row * C::kEpiPitch + col);
+      const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(epi + row * C::kEpiPitch + col + 4);
+      float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      u32x4_t out;
+      if constexpr (OP == OP_APPLY) {
+        const u32x4_t xe = *reinterpret_cast<const u32x4_t*>(Eb + (int64_t)gi * p.lde + gj);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float ax0 = p.alpha * bf16_to_f32(xe[e] & 0xFFFFu);
+          const float ax1 = p.alpha * bf16_to_f32(xe[e] >> 16);
+          float r0, r1;
           if (p.split) {
-            o = f32_to_bf16(bf16_to_f32(f32_to_bf16(v)) + ax);
+            r0 = bf16_to_f32(f32_to_bf16(v[2 * e])) + ax0;
+            r1 = bf16_to_f32(f32_to_bf16(v[2 * e + 1])) + ax1;
           } else {
-            o = f32_to_bf16(ax + v);
+            r0 = ax0 + v[2 * e];
+            r1 = ax1 + v[2 * e + 1];
           }
-          Cb[(int64_t)gi * p.ldc + gj] = static_cast<uint16_t>(o);
+          out[e] = pack_bf16x2(r0, r1);
+        }
+        *reinterpret_cast<u32x4_t*>(Cb + (int64_t)gi * p.ldc + gj) = out;
+      } else {
+        if constexpr (OP == OP_POLY) {
+          const u32x4_t ae = *reinterpret_cast<const u32x4_t*>(Eb + (int64_t)gi * p.lde + gj);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float ba0 = p.alpha * bf16_to_f32(ae[e] & 0xFFFFu);
+            const float ba1 = p.alpha * bf16_to_f32(ae[e] >> 16);
+            const float cq0 = p.beta * v[2 * e];
+            const float cq1 = p.beta * v[2 * e + 1];
+            v[2 * e] = ba0 + cq0;
+            v[2 * e + 1] = ba1 + cq1;
+          }
+          // the mirror pass below reads the combined value back
+          *reinterpret_cast<f32x4_t*>(epi + row * C::kEpiPitch + col) =
+              f32x4_t{v[0], v[1], v[2], v[3]};
+          *reinterpret_cast<f32x4_t*>(epi + row * C::kEpiPitch + col + 4) =
+              f32x4_t{v[4], v[5], v[6], v[7]};
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
+        if (!diag_tile) {
+          *reinterpret_cast<u32x4_t*>(Cb + (int64_t)gi * p.ldc + gj) = out;
         } else {
-          if (ti == tj && gi > gj) continue;
-          float w = v;
-          if constexpr (OP == OP_POLY) {
-            const float ba = p.alpha * bf16_to_f32(Eb[(int64_t)gi * p.lde + gj]);
-            const float cq = p.beta * v;
-            w = ba + cq;
+          // diagonal tile: entries with gi <= gj only (the mirror pass writes the rest)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            if (gi <= gj + e) {
+              const uint32_t w = out[e >> 1];
+              Cb[(int64_t)gi * p.ldc + gj + e] = (uint16_t)((e & 1) ? (w >> 16) : (w & 0xFFFFu));
+            }
           }
-          const uint32_t o = f32_to_bf16(w);
-          Cb[(int64_t)gi * p.ldc + gj] = static_cast<uint16_t>(o);
-          Cb[(int64_t)gj * p.ldc + gi] = static_cast<uint16_t>(o);
           if constexpr (OP == OP_GRAM) {
-            if (gi == gj) tsum += bf16_to_f32(o);
+            if (gi >= gj && gi < gj + 8) {
+              const uint32_t w = out[(gi - gj) >> 1];
+              tsum += bf16_to_f32(((gi - gj) & 1) ? (w >> 16) : (w & 0xFFFFu));
+            }
           }
         }
       }
     }
+
+    if constexpr (OP != OP_APPLY) {
+      wait_lds();
+      __builtin_amdgcn_wave_barrier();
+      // mirror: C[gj][gi .. gi+7] from LDS column gj, rows gi .. gi+7 (8-row groups)
+#pragma unroll
+      for (int pass = 0; pass < (C::kWTN * 4) / 64; ++pass) {
+        const int item = pass * 64 + lane;
+        const int col = item % C::kWTN;
+        const int rq = item / C::kWTN;
+        const int gj = gj0 + col;
+        const int gi = gi0 + rq * 8;
+        if (gj >= p.N || gi >= p.M) continue;
+        if (diag_tile && gj < gi + 8) {
+          // entries with gi + e < gj only (gi + e == gj was stored directly)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            if (gi + e < gj) {
+              const float x = epi[(rq * 8 + e) * C::kEpiPitch + col];
+              Cb[(int64_t)gj * p.ldc + gi + e] = (uint16_t)f32_to_bf16(x);
+            }
+          }
+          continue;
+        }
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = epi[(rq * 8 + e) * C::kEpiPitch + col];
+        u32x4_t out;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
+        *reinterpret_cast<u32x4_t*>(Cb + (int64_t)gj * p.ldc + gi) = out;
+      }
+    }
+    wait_lds();
+    __builtin_amdgcn_wave_barrier();
   }
 
   if constexpr (OP == OP_GRAM) {
-    if (p.trace != nullptr && ti == tj) {
-      // fixed-order reduction: butterfly within each wave, then waves 0..3 in order
+    if (p.trace != nullptr && diag_tile) {
+      // fixed-order reduction: butterfly within each wave, then waves in index order
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) tsum += __shfl_xor(tsum, off, 64);
       if (lane == 0) sRed[wave] = tsum;
       __syncthreads();
       if (tid == 0) {
-        float t = 0.0f;
-        for (int w = 0; w < kThreads / 64; ++w) t += sRed[w];
-        p.trace[b * p.trace_slots + ti] = t;
+        float s = 0.0f;
+        for (int w = 0; w < C::kWaves; ++w) s += sRed[w];
+        p.trace[b * p.trace_slots + ti] = s;
       }
     }
   }
@@ -329,16 +496,28 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmParams p) {
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-template <int OP, bool PT, bool QT>
-hipError_t launch(const GemmParams& p, int64_t g, int tiles, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_kernel<OP, PT, QT>), dim3((unsigned)tiles, (unsigned)g), dim3(kThreads),
-                     0, stream, p);
+template <int OP, bool PT, bool QT, int BM, int BN, int WM, int WN, int STAGES>
+hipError_t launch(GemmParams p, int64_t g, hipStream_t stream) {
+  using C = Cfg<BM, BN, WM, WN, STAGES>;
+  auto kern = gemm_kernel<OP, PT, QT, BM, BN, WM, WN, STAGES>;
+  static bool configured = false;   // raise the dynamic LDS limit once per instantiation
+  if (!configured) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  p.total = (int)(p.tiles * g);
+  hipLaunchKernelGGL(kern, dim3((unsigned)p.total), dim3(C::kThreads), C::kLdsBytes, stream, p);
   return hipGetLastError();
 }
 
+// Gram and polynomial: 128x128 tiles (2x2 waves of 64x64), three LDS stages.
+constexpr int kSymTile = 128;
+
 }  // namespace
 
-int gram_trace_slots(int s) { return ceil_div(s, kBM); }
+int gram_trace_slots(int s) { return ceil_div(s, kSymTile); }
 
 hipError_t launch_gram(const uint16_t* x, uint16_t* a, float* trace_partials, const Shape& sh,
                        hipStream_t stream) {
@@ -347,6 +526,7 @@ hipError_t launch_gram(const uint16_t* x, uint16_t* a, float* trace_partials, co
   p.P = x;
   p.Q = x;
   p.strideP = p.strideQ = (int64_t)sh.m * sh.n;
+  p.bytesP = p.bytesQ = (uint32_t)((int64_t)sh.m * sh.n * 2);
   p.ldp = p.ldq = sh.n;
   p.M = p.N = s;
   p.K = sh.L();
@@ -355,10 +535,10 @@ hipError_t launch_gram(const uint16_t* x, uint16_t* a, float* trace_partials, co
   p.ldc = s;
   p.trace = trace_partials;
   p.trace_slots = gram_trace_slots(s);
-  p.tiles_m = p.tiles_n = ceil_div(s, kBM);
-  const int tiles = p.tiles_m * (p.tiles_m + 1) / 2;
-  if (sh.tall()) return launch<OP_GRAM, true, true>(p, sh.g, tiles, stream);
-  return launch<OP_GRAM, false, false>(p, sh.g, tiles, stream);
+  p.tiles_m = p.tiles_n = ceil_div(s, kSymTile);
+  p.tiles = p.tiles_m * (p.tiles_m + 1) / 2;
+  if (sh.tall()) return launch<OP_GRAM, true, true, 128, 128, 2, 2, 3>(p, sh.g, stream);
+  return launch<OP_GRAM, false, false, 128, 128, 2, 2, 3>(p, sh.g, stream);
 }
 
 hipError_t launch_poly(const uint16_t* a, uint16_t* bout, float coef_b, float coef_c, int64_t g,
@@ -367,6 +547,7 @@ hipError_t launch_poly(const uint16_t* a, uint16_t* bout, float coef_b, float co
   p.P = a;
   p.Q = a;
   p.strideP = p.strideQ = (int64_t)s * s;
+  p.bytesP = p.bytesQ = (uint32_t)((int64_t)s * s * 2);
   p.ldp = p.ldq = s;
   p.M = p.N = p.K = s;
   p.C = bout;
@@ -377,9 +558,9 @@ hipError_t launch_poly(const uint16_t* a, uint16_t* bout, float coef_b, float co
   p.lde = s;
   p.alpha = coef_b;
   p.beta = coef_c;
-  p.tiles_m = p.tiles_n = ceil_div(s, kBM);
-  const int tiles = p.tiles_m * (p.tiles_m + 1) / 2;
-  return launch<OP_POLY, false, false>(p, g, tiles, stream);
+  p.tiles_m = p.tiles_n = ceil_div(s, kSymTile);
+  p.tiles = p.tiles_m * (p.tiles_m + 1) / 2;
+  return launch<OP_POLY, false, false, 128, 128, 2, 2, 3>(p, g, stream);
 }
 
 hipError_t launch_apply(const uint16_t* x, const uint16_t* bm, uint16_t* c, float coef_a,
@@ -396,29 +577,34 @@ hipError_t launch_apply(const uint16_t* x, const uint16_t* bm, uint16_t* c, floa
   p.lde = sh.n;
   p.alpha = coef_a;
   p.split = split ? 1 : 0;
-  p.tiles_m = ceil_div(sh.m, kBM);
-  p.tiles_n = ceil_div(sh.n, kBN);
-  const int tiles = p.tiles_m * p.tiles_n;
+  constexpr int BM = 128, BN = 128;
+  p.tiles_m = ceil_div(sh.m, BM);
+  p.tiles_n = ceil_div(sh.n, BN);
+  p.tiles = p.tiles_m * p.tiles_n;
   if (sh.tall()) {
     // C = a X + X B: P = X rows (K = n contiguous), Q = rows of symmetric B
     p.P = x;
     p.strideP = (int64_t)sh.m * sh.n;
+    p.bytesP = (uint32_t)((int64_t)sh.m * sh.n * 2);
     p.ldp = sh.n;
     p.Q = bm;
     p.strideQ = (int64_t)s * s;
+    p.bytesQ = (uint32_t)((int64_t)s * s * 2);
     p.ldq = s;
     p.K = sh.n;
-    return launch<OP_APPLY, false, false>(p, sh.g, tiles, stream);
+    return launch<OP_APPLY, false, false, BM, BN, 2, 2, 3>(p, sh.g, stream);
   }
-  // C = a X + B X: P = rows of B (K = m contiguous), Q(j, k) = X[k][j] (K-strided)
+  // C = a X + B X: P = rows of B (K = m contiguous), Q(j, k) = X[k][j] (K-major)
   p.P = bm;
   p.strideP = (int64_t)s * s;
+  p.bytesP = (uint32_t)((int64_t)s * s * 2);
   p.ldp = s;
   p.Q = x;
   p.strideQ = (int64_t)sh.m * sh.n;
+  p.bytesQ = (uint32_t)((int64_t)sh.m * sh.n * 2);
   p.ldq = sh.n;
   p.K = sh.m;
-  return launch<OP_APPLY, false, true>(p, sh.g, tiles, stream);
+  return launch<OP_APPLY, false, true, BM, BN, 2, 2, 3>(p, sh.g, stream);
 }
 
 }  // namespace anvil
