@@ -512,8 +512,20 @@ hipError_t launch(GemmParams p, int64_t g, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Gram and polynomial: 128x128 tiles (2x2 waves of 64x64), three LDS stages.
+// Gram and polynomial: 128x128 tiles (2x2 waves of 64x64), two LDS stages (64 KB), so two
+// workgroups share a CU and hide each other's slab latency.
 constexpr int kSymTile = 128;
+#ifndef ANVIL_SYM_STAGES
+#define ANVIL_SYM_STAGES 2
+#endif
+// Apply: 128x256 tiles (2x4 waves of 64x64), two LDS stages (96 KB).
+#ifndef ANVIL_APPLY_BM
+#define ANVIL_APPLY_BM 128
+#define ANVIL_APPLY_BN 256
+#define ANVIL_APPLY_WM 2
+#define ANVIL_APPLY_WN 4
+#define ANVIL_APPLY_STAGES 2
+#endif
 
 }  // namespace
 
@@ -537,8 +549,8 @@ hipError_t launch_gram(const uint16_t* x, uint16_t* a, float* trace_partials, co
   p.trace_slots = gram_trace_slots(s);
   p.tiles_m = p.tiles_n = ceil_div(s, kSymTile);
   p.tiles = p.tiles_m * (p.tiles_m + 1) / 2;
-  if (sh.tall()) return launch<OP_GRAM, true, true, 128, 128, 2, 2, 3>(p, sh.g, stream);
-  return launch<OP_GRAM, false, false, 128, 128, 2, 2, 3>(p, sh.g, stream);
+  if (sh.tall()) return launch<OP_GRAM, true, true, 128, 128, 2, 2, ANVIL_SYM_STAGES>(p, sh.g, stream);
+  return launch<OP_GRAM, false, false, 128, 128, 2, 2, ANVIL_SYM_STAGES>(p, sh.g, stream);
 }
 
 hipError_t launch_poly(const uint16_t* a, uint16_t* bout, float coef_b, float coef_c, int64_t g,
@@ -560,7 +572,7 @@ hipError_t launch_poly(const uint16_t* a, uint16_t* bout, float coef_b, float co
   p.beta = coef_c;
   p.tiles_m = p.tiles_n = ceil_div(s, kSymTile);
   p.tiles = p.tiles_m * (p.tiles_m + 1) / 2;
-  return launch<OP_POLY, false, false, 128, 128, 2, 2, 3>(p, g, stream);
+  return launch<OP_POLY, false, false, 128, 128, 2, 2, ANVIL_SYM_STAGES>(p, g, stream);
 }
 
 hipError_t launch_apply(const uint16_t* x, const uint16_t* bm, uint16_t* c, float coef_a,
@@ -577,7 +589,7 @@ hipError_t launch_apply(const uint16_t* x, const uint16_t* bm, uint16_t* c, floa
   p.lde = sh.n;
   p.alpha = coef_a;
   p.split = split ? 1 : 0;
-  constexpr int BM = 128, BN = 128;
+  constexpr int BM = ANVIL_APPLY_BM, BN = ANVIL_APPLY_BN;
   p.tiles_m = ceil_div(sh.m, BM);
   p.tiles_n = ceil_div(sh.n, BN);
   p.tiles = p.tiles_m * p.tiles_n;
@@ -592,7 +604,7 @@ hipError_t launch_apply(const uint16_t* x, const uint16_t* bm, uint16_t* c, floa
     p.bytesQ = (uint32_t)((int64_t)s * s * 2);
     p.ldq = s;
     p.K = sh.n;
-    return launch<OP_APPLY, false, false, BM, BN, 2, 2, 3>(p, sh.g, stream);
+    return launch<OP_APPLY, false, false, BM, BN, ANVIL_APPLY_WM, ANVIL_APPLY_WN, ANVIL_APPLY_STAGES>(p, sh.g, stream);
   }
   // C = a X + B X: P = rows of B (K = m contiguous), Q(j, k) = X[k][j] (K-major)
   p.P = bm;
@@ -604,7 +616,7 @@ hipError_t launch_apply(const uint16_t* x, const uint16_t* bm, uint16_t* c, floa
   p.bytesQ = (uint32_t)((int64_t)sh.m * sh.n * 2);
   p.ldq = sh.n;
   p.K = sh.m;
-  return launch<OP_APPLY, false, true, BM, BN, 2, 2, 3>(p, sh.g, stream);
+  return launch<OP_APPLY, false, true, BM, BN, ANVIL_APPLY_WM, ANVIL_APPLY_WN, ANVIL_APPLY_STAGES>(p, sh.g, stream);
 }
 
 }  // namespace anvil
