@@ -56,7 +56,6 @@ namespace {
 
 enum { OP_GRAM = 0, OP_POLY = 1, OP_APPLY = 2 };
 
-constexpr int kBK = 64;                  // K per slab
 constexpr uint32_t kOOB = 0x80000000u;   // buffer offset past any range: the load returns 0
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -92,17 +91,20 @@ struct GemmParams {
 // LDS slab layouts
 // ---------------------------------------------------------------------------------------------
 
-// [ROWS][64] bf16: a row is 128 bytes = 8 slots of 16 bytes (8 k each).  Logical slot c of row r
-// sits at slot c ^ ((r >> 1) & 7): 16 consecutive rows read at one logical slot hit 16 distinct
+// [ROWS][BK] bf16: a row is BK*2 bytes = BK/8 slots of 16 bytes (8 k each), and 256 bytes of LDS
+// (one pass over the 64 banks) hold 16/(BK/8) rows.  Logical slot c of row r sits at slot
+// c ^ ((r / rows_per_256B) % slots): 16 consecutive rows read at one logical slot hit 16 distinct
 // 16-byte bank groups.
-template <int ROWS>
+template <int ROWS, int BK>
 struct KContig {
+  static constexpr int kSlots = BK / 8;
+  static constexpr int kRowsPer256 = 16 / kSlots;
   __device__ static __forceinline__ int offset(int row, int c) {
-    return row * 128 + ((c ^ ((row >> 1) & 7)) << 4);
+    return row * (BK * 2) + ((c ^ ((row / kRowsPer256) % kSlots)) << 4);
   }
 };
 
-// [64][ROWS] bf16: a k-row is ROWS*2 bytes = ROWS/8 slots.  Logical slot c of k-row kr sits at
+// [BK][ROWS] bf16: a k-row is ROWS*2 bytes = ROWS/8 slots.  Logical slot c of k-row kr sits at
 // slot c ^ (4 * (kr & 3)).
 template <int ROWS>
 struct KMajor {
@@ -140,21 +142,24 @@ __device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t lds, uint32_t voff)
                : "memory", "m0");
 }
 
-// Issue the DMA of one slab of an operand (rows row0.., k0..k0+63) into LDS at `dst`.  The slab
-// is ROWS/8 wave-instructions of 1 KB; instruction u lands at dst + u*1024, lane L's 16 bytes at
-// dst + u*1024 + 16*L.
-template <bool KMAJOR, int ROWS, int NW>
+// Issue the DMA of one slab of an operand (rows row0.., k0..k0+BK-1) into LDS at `dst`.  The slab
+// is ROWS*BK/512 wave-instructions of 1 KB; instruction u lands at dst + u*1024, lane L's 16 bytes
+// at dst + u*1024 + 16*L.
+template <bool KMAJOR, int ROWS, int BK, int NW>
 __device__ __forceinline__ void issue_slab(i32x4_t rsrc, const char* dst, int ld,
                                            int row0, int rows, int k0, int K, int wave,
                                            int lane) {
-  static_assert((ROWS / 8) % NW == 0, "slab instructions must split evenly over the waves");
+  constexpr int kInsts = ROWS * BK / 512;
+  static_assert(kInsts % NW == 0, "slab instructions must split evenly over the waves");
 #pragma unroll
-  for (int i = 0; i < ROWS / 8 / NW; ++i) {
+  for (int i = 0; i < kInsts / NW; ++i) {
     const int u = wave + i * NW;
     uint32_t voff;
     if constexpr (!KMAJOR) {
-      const int row = 8 * u + (lane >> 3);
-      const int c = (lane & 7) ^ ((row >> 1) & 7);
+      constexpr int kSlots = BK / 8;
+      constexpr int kRowsPerInst = 64 / kSlots;
+      const int row = kRowsPerInst * u + lane / kSlots;
+      const int c = (lane % kSlots) ^ ((row / KContig<ROWS, BK>::kRowsPer256) % kSlots);
       const int gr = row0 + row;
       const int gk = k0 + c * 8;
       voff = (gr < rows && gk < K) ? (uint32_t)(gr * ld + gk) * 2u : kOOB;
@@ -173,12 +178,12 @@ __device__ __forceinline__ void issue_slab(i32x4_t rsrc, const char* dst, int ld
 
 // MFMA operand of a 32-row fragment (rows R0..R0+31) at k-step ks (k = 16ks .. 16ks+15):
 // lane l holds row R0 + l%32, k = 16ks + 8(l/32) + 0..7.
-template <bool KMAJOR, int ROWS>
+template <bool KMAJOR, int ROWS, int BK>
 __device__ __forceinline__ bf16x8_t read_frag(const char* tile, int R0, int ks, int lane) {
   if constexpr (!KMAJOR) {
     const int row = R0 + (lane & 31);
     const int c = 2 * ks + (lane >> 5);
-    return *reinterpret_cast<const bf16x8_t*>(tile + KContig<ROWS>::offset(row, c));
+    return *reinterpret_cast<const bf16x8_t*>(tile + KContig<ROWS, BK>::offset(row, c));
   } else {
     const int grp = lane >> 4;
     const int r = lane & 15;
@@ -228,7 +233,7 @@ __device__ __forceinline__ void upper_tile(int t, int tiles, int* ti, int* tj) {
   *tj = i + t;
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES>
+template <int BM, int BN, int WM, int WN, int STAGES, int BK>
 struct Cfg {
   static constexpr int kWaves = WM * WN;
   static constexpr int kThreads = kWaves * 64;
@@ -236,21 +241,23 @@ struct Cfg {
   static constexpr int kWTN = BN / WN;   // wave tile cols
   static constexpr int kFM = kWTM / 32;
   static constexpr int kFN = kWTN / 32;
-  static constexpr int kStageBytes = (BM + BN) * 128;
+  static constexpr int kStageBytes = (BM + BN) * BK * 2;
+  static constexpr int kQOffset = BM * BK * 2;
   static constexpr int kEpiPitch = kWTN + 4;                  // fp32 per LDS epilogue row
   static constexpr int kEpiBytes = kWaves * 32 * kEpiPitch * 4;
   static constexpr int kLdsBytes =
       (STAGES * kStageBytes > kEpiBytes ? STAGES * kStageBytes : kEpiBytes);
-  static constexpr int kLoadsPerSlab = (BM / 8 + BN / 8) / kWaves;
-  static_assert(kWTM % 32 == 0 && kWTN % 32 == 0, "wave tile must be whole 32x32 fragments");
   static_assert(kWTN % 8 == 0 && 64 % (kWTN / 8) == 0, "epilogue moves 8 columns per lane");
+  static constexpr int kLoadsPerSlab = (BM + BN) * BK / 512 / kWaves;
+  static_assert(BK == 32 || BK == 64, "slab depth");
+  static_assert(kWTM % 32 == 0 && kWTN % 32 == 0, "wave tile must be whole 32x32 fragments");
   static_assert(STAGES >= 2, "at least double buffering");
   static_assert(kLoadsPerSlab * (STAGES - 2) < 64, "vmcnt range");
 };
 
-template <int OP, bool PT, bool QT, int BM, int BN, int WM, int WN, int STAGES>
+template <int OP, bool PT, bool QT, int BM, int BN, int WM, int WN, int STAGES, int BK, bool SLAB>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
-  using C = Cfg<BM, BN, WM, WN, STAGES>;
+  using C = Cfg<BM, BN, WM, WN, STAGES, BK>;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   __shared__ float sRed[C::kWaves];
 
@@ -284,17 +291,38 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[fm][fn][r] = 0.0f;
 
-  const int KT = (p.K + kBK - 1) / kBK;
+  const int KT = (p.K + BK - 1) / BK;
 
   // prologue: slabs 0 .. STAGES-2 in flight
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s) {
     if (s < KT) {
       char* st = smem + s * C::kStageBytes;
-      issue_slab<PT, BM, C::kWaves>(rP, st, p.ldp, i0, p.M, s * kBK, p.K, wave, lane);
-      issue_slab<QT, BN, C::kWaves>(rQ, st + BM * 128, p.ldq, j0, p.N, s * kBK, p.K, wave, lane);
+      issue_slab<PT, BM, BK, C::kWaves>(rP, st, p.ldp, i0, p.M, s * BK, p.K, wave, lane);
+      issue_slab<QT, BN, BK, C::kWaves>(rQ, st + C::kQOffset, p.ldq, j0, p.N, s * BK, p.K, wave,
+                                        lane);
     }
   }
+
+  // Epilogue operand (X for the apply, A for the polynomial), fetched one 32-row block ahead of
+  // its use (the first block during the last slab) so that the load latency overlaps other work.
+  // Lane mapping as in the epilogue's direct pass: 8 consecutive columns of one row.
+  constexpr int kLanesPerRow = C::kWTN / 8;
+  constexpr int kRowsPerPass = 64 / kLanesPerRow;
+  constexpr int kPasses = 32 / kRowsPerPass;
+  constexpr bool kHasE = OP != OP_GRAM;
+  const uint16_t* Eb = p.E ? p.E + b * p.strideE : nullptr;
+  u32x4_t ecur[kHasE ? kPasses : 1];
+  auto load_e = [&](u32x4_t* dst, int fm) {
+#pragma unroll
+    for (int pass = 0; pass < kPasses; ++pass) {
+      const int gi = i0 + wm * C::kWTM + fm * 32 + pass * kRowsPerPass + lane / kLanesPerRow;
+      const int gj = j0 + wn * C::kWTN + (lane % kLanesPerRow) * 8;
+      dst[pass] = (gi < p.M && gj < p.N)
+                      ? *reinterpret_cast<const u32x4_t*>(Eb + (int64_t)gi * p.lde + gj)
+                      : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
 
   for (int kt = 0; kt < KT; ++kt) {
     // slab kt has landed once at most STAGES-2 younger slabs of this wave are still in flight
@@ -308,61 +336,85 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
       const int kn = kt + STAGES - 1;
       if (kn < KT) {
         char* st = smem + (kn % STAGES) * C::kStageBytes;
-        issue_slab<PT, BM, C::kWaves>(rP, st, p.ldp, i0, p.M, kn * kBK, p.K, wave, lane);
-        issue_slab<QT, BN, C::kWaves>(rQ, st + BM * 128, p.ldq, j0, p.N, kn * kBK, p.K, wave,
-                                      lane);
+        issue_slab<PT, BM, BK, C::kWaves>(rP, st, p.ldp, i0, p.M, kn * BK, p.K, wave, lane);
+        issue_slab<QT, BN, BK, C::kWaves>(rQ, st + C::kQOffset, p.ldq, j0, p.N, kn * BK, p.K,
+                                          wave, lane);
       }
     }
+    if constexpr (kHasE) {
+      if (kt == KT - 1) load_e(ecur, 0);
+    }
     const char* tp = smem + (kt % STAGES) * C::kStageBytes;
-    const char* tq = tp + BM * 128;
+    const char* tq = tp + C::kQOffset;
 
-    f32x16_t slab[C::kFM][C::kFN];
-#pragma unroll
-    for (int fm = 0; fm < C::kFM; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < C::kFN; ++fn)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) slab[fm][fn][r] = 0.0f;
-#pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      bf16x8_t fa[C::kFM], fb[C::kFN];
-#pragma unroll
-      for (int fm = 0; fm < C::kFM; ++fm)
-        fa[fm] = read_frag<PT, BM>(tp, wm * C::kWTM + fm * 32, ks, lane);
-#pragma unroll
-      for (int fn = 0; fn < C::kFN; ++fn)
-        fb[fn] = read_frag<QT, BN>(tq, wn * C::kWTN + fn * 32, ks, lane);
+    // SLAB: this slab accumulates into fresh registers, added to the running sums afterwards;
+    // otherwise the MFMAs accumulate into the running sums directly.
+    f32x16_t slab[SLAB ? C::kFM : 1][SLAB ? C::kFN : 1];
+    if constexpr (SLAB) {
 #pragma unroll
       for (int fm = 0; fm < C::kFM; ++fm)
 #pragma unroll
         for (int fn = 0; fn < C::kFN; ++fn)
-          slab[fm][fn] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[fm], fb[fn], slab[fm][fn], 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) slab[fm][fn][r] = 0.0f;
     }
 #pragma unroll
-    for (int fm = 0; fm < C::kFM; ++fm)
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8_t fa[C::kFM], fb[C::kFN];
 #pragma unroll
-      for (int fn = 0; fn < C::kFN; ++fn) acc[fm][fn] += slab[fm][fn];
+      for (int fm = 0; fm < C::kFM; ++fm)
+        fa[fm] = read_frag<PT, BM, BK>(tp, wm * C::kWTM + fm * 32, ks, lane);
+#pragma unroll
+      for (int fn = 0; fn < C::kFN; ++fn)
+        fb[fn] = read_frag<QT, BN, BK>(tq, wn * C::kWTN + fn * 32, ks, lane);
+#pragma unroll
+      for (int fm = 0; fm < C::kFM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < C::kFN; ++fn) {
+          if constexpr (SLAB) {
+            slab[fm][fn] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[fn], fa[fm], slab[fm][fn], 0, 0, 0);
+          } else {
+            acc[fm][fn] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[fn], fa[fm], acc[fm][fn], 0, 0, 0);
+          }
+        }
+    }
+    if constexpr (SLAB) {
+#pragma unroll
+      for (int fm = 0; fm < C::kFM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < C::kFN; ++fn) acc[fm][fn] += slab[fm][fn];
+    }
   }
   __syncthreads();   // every wave is done with the operand ring; reuse it for the epilogue
 
   // ---------------- epilogue: per wave, 32 rows at a time through LDS ----------------
+  // With the MFMA operands as (Q, P) the fragment holds C transposed: register r of lane l is
+  // C[i][j] with i = l%32 and j = 8(r/4) + 4(l/32) + r%4, i.e. runs of 4 consecutive columns of
+  // one row, which go to LDS as one 16-byte write.  The rows then leave LDS 8 columns per lane
+  // and go to memory as coalesced 16-byte stores; the mirror of a symmetric tile is read down the
+  // LDS columns and also leaves as 16-byte stores.
   float* epi = reinterpret_cast<float*>(smem) + wave * 32 * C::kEpiPitch;
   uint16_t* Cb = p.C + b * p.strideC;
-  const uint16_t* Eb = p.E ? p.E + b * p.strideE : nullptr;
   const bool diag_tile = (OP != OP_APPLY) && ti == tj;
   float tsum = 0.0f;
 
 #pragma unroll
   for (int fm = 0; fm < C::kFM; ++fm) {
-    // accumulators -> LDS (fp32): register r of lane l is row 8(r/4) + 4(l/32) + r%4, col l%32
+    u32x4_t enext[kHasE ? kPasses : 1];
+    if constexpr (kHasE) {
+      if (fm + 1 < C::kFM) load_e(enext, fm + 1);
+    }
 #pragma unroll
     for (int fn = 0; fn < C::kFN; ++fn)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int col = fn * 32 + (lane & 31);
-        epi[row * C::kEpiPitch + col] = acc[fm][fn][r];
+      for (int q = 0; q < 4; ++q) {
+        const int row = lane & 31;
+        const int col = fn * 32 + 8 * q + 4 * (lane >> 5);
+        *reinterpret_cast<f32x4_t*>(epi + row * C::kEpiPitch + col) =
+            f32x4_t{acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1], acc[fm][fn][4 * q + 2],
+                    acc[fm][fn][4 * q + 3]};
       }
     wait_lds();
     __builtin_amdgcn_wave_barrier();
@@ -371,10 +423,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
     const int gj0 = j0 + wn * C::kWTN;             // first global col of this wave
 
     // direct rows: each lane takes 8 consecutive columns of one row
-    constexpr int kLanesPerRow = C::kWTN / 8;
-    constexpr int kRowsPerPass = 64 / kLanesPerRow;
 #pragma unroll
-    for (int pass = 0; pass < 32 / kRowsPerPass; ++pass) {
+    for (int pass = 0; pass < kPasses; ++pass) {
       const int row = pass * kRowsPerPass + lane / kLanesPerRow;
       const int col = (lane % kLanesPerRow) * 8;
       const int gi = gi0 + row;
@@ -385,7 +435,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
       float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
       u32x4_t out;
       if constexpr (OP == OP_APPLY) {
-        const u32x4_t xe = *reinterpret_cast<const u32x4_t*>(Eb + (int64_t)gi * p.lde + gj);
+        const u32x4_t xe = ecur[pass];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float ax0 = p.alpha * bf16_to_f32(xe[e] & 0xFFFFu);
@@ -403,7 +453,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
         *reinterpret_cast<u32x4_t*>(Cb + (int64_t)gi * p.ldc + gj) = out;
       } else {
         if constexpr (OP == OP_POLY) {
-          const u32x4_t ae = *reinterpret_cast<const u32x4_t*>(Eb + (int64_t)gi * p.lde + gj);
+          const u32x4_t ae = ecur[pass];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float ba0 = p.alpha * bf16_to_f32(ae[e] & 0xFFFFu);
@@ -476,6 +526,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
     }
     wait_lds();
     __builtin_amdgcn_wave_barrier();
+    if constexpr (kHasE) {
+      if (fm + 1 < C::kFM) {
+#pragma unroll
+        for (int pass = 0; pass < kPasses; ++pass) ecur[pass] = enext[pass];
+      }
+    }
   }
 
   if constexpr (OP == OP_GRAM) {
@@ -496,10 +552,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-template <int OP, bool PT, bool QT, int BM, int BN, int WM, int WN, int STAGES>
+template <int OP, bool PT, bool QT, int BM, int BN, int WM, int WN, int STAGES, int BK, bool SLAB>
 hipError_t launch(GemmParams p, int64_t g, hipStream_t stream) {
-  using C = Cfg<BM, BN, WM, WN, STAGES>;
-  auto kern = gemm_kernel<OP, PT, QT, BM, BN, WM, WN, STAGES>;
+  using C = Cfg<BM, BN, WM, WN, STAGES, BK>;
+  auto kern = gemm_kernel<OP, PT, QT, BM, BN, WM, WN, STAGES, BK, SLAB>;
   static bool configured = false;   // raise the dynamic LDS limit once per instantiation
   if (!configured) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -512,20 +568,16 @@ hipError_t launch(GemmParams p, int64_t g, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Gram and polynomial: 128x128 tiles (2x2 waves of 64x64), two LDS stages (64 KB), so two
-// workgroups share a CU and hide each other's slab latency.
+// Tile configurations (measured on MI355X over the five bank shapes):
+//  * Gram and polynomial: 128x128 tiles, 2x2 waves of 64x64, 64-deep slabs, two LDS stages
+//    (64 KB), so two workgroups share a CU.  The Gram accumulates per slab (long K); the
+//    polynomial (K = s) accumulates directly.
+//  * Apply: 128x256 tiles, 2x2 waves of 64x128, 32-deep slabs, three stages (72 KB, two
+//    workgroups per CU) when the stack fills at least one full round of 512 workgroups;
+//    otherwise 128x128 tiles (2x2 waves of 64x64, 64-deep slabs, two stages), which keep more
+//    CUs busy on small stacks.
 constexpr int kSymTile = 128;
-#ifndef ANVIL_SYM_STAGES
-#define ANVIL_SYM_STAGES 2
-#endif
-// Apply: 128x256 tiles (2x4 waves of 64x64), two LDS stages (96 KB).
-#ifndef ANVIL_APPLY_BM
-#define ANVIL_APPLY_BM 128
-#define ANVIL_APPLY_BN 256
-#define ANVIL_APPLY_WM 2
-#define ANVIL_APPLY_WN 4
-#define ANVIL_APPLY_STAGES 2
-#endif
+constexpr int kFullRound = 512;
 
 }  // namespace
 
@@ -549,8 +601,8 @@ hipError_t launch_gram(const uint16_t* x, uint16_t* a, float* trace_partials, co
   p.trace_slots = gram_trace_slots(s);
   p.tiles_m = p.tiles_n = ceil_div(s, kSymTile);
   p.tiles = p.tiles_m * (p.tiles_m + 1) / 2;
-  if (sh.tall()) return launch<OP_GRAM, true, true, 128, 128, 2, 2, ANVIL_SYM_STAGES>(p, sh.g, stream);
-  return launch<OP_GRAM, false, false, 128, 128, 2, 2, ANVIL_SYM_STAGES>(p, sh.g, stream);
+  if (sh.tall()) return launch<OP_GRAM, true, true, 128, 128, 2, 2, 2, 64, true>(p, sh.g, stream);
+  return launch<OP_GRAM, false, false, 128, 128, 2, 2, 2, 64, true>(p, sh.g, stream);
 }
 
 hipError_t launch_poly(const uint16_t* a, uint16_t* bout, float coef_b, float coef_c, int64_t g,
@@ -572,11 +624,12 @@ hipError_t launch_poly(const uint16_t* a, uint16_t* bout, float coef_b, float co
   p.beta = coef_c;
   p.tiles_m = p.tiles_n = ceil_div(s, kSymTile);
   p.tiles = p.tiles_m * (p.tiles_m + 1) / 2;
-  return launch<OP_POLY, false, false, 128, 128, 2, 2, ANVIL_SYM_STAGES>(p, g, stream);
+  return launch<OP_POLY, false, false, 128, 128, 2, 2, 2, 64, false>(p, g, stream);
 }
 
-hipError_t launch_apply(const uint16_t* x, const uint16_t* bm, uint16_t* c, float coef_a,
-                        bool split, const Shape& sh, hipStream_t stream) {
+template <int BM, int BN, int WM, int WN, int STAGES, int BK>
+hipError_t launch_apply_cfg(const uint16_t* x, const uint16_t* bm, uint16_t* c, float coef_a,
+                            bool split, const Shape& sh, hipStream_t stream) {
   const int s = sh.s();
   GemmParams p{};
   p.M = sh.m;
@@ -589,7 +642,6 @@ hipError_t launch_apply(const uint16_t* x, const uint16_t* bm, uint16_t* c, floa
   p.lde = sh.n;
   p.alpha = coef_a;
   p.split = split ? 1 : 0;
-  constexpr int BM = ANVIL_APPLY_BM, BN = ANVIL_APPLY_BN;
   p.tiles_m = ceil_div(sh.m, BM);
   p.tiles_n = ceil_div(sh.n, BN);
   p.tiles = p.tiles_m * p.tiles_n;
@@ -604,7 +656,7 @@ hipError_t launch_apply(const uint16_t* x, const uint16_t* bm, uint16_t* c, floa
     p.bytesQ = (uint32_t)((int64_t)s * s * 2);
     p.ldq = s;
     p.K = sh.n;
-    return launch<OP_APPLY, false, false, BM, BN, ANVIL_APPLY_WM, ANVIL_APPLY_WN, ANVIL_APPLY_STAGES>(p, sh.g, stream);
+    return launch<OP_APPLY, false, false, BM, BN, WM, WN, STAGES, BK, false>(p, sh.g, stream);
   }
   // C = a X + B X: P = rows of B (K = m contiguous), Q(j, k) = X[k][j] (K-major)
   p.P = bm;
@@ -616,7 +668,15 @@ hipError_t launch_apply(const uint16_t* x, const uint16_t* bm, uint16_t* c, floa
   p.bytesQ = (uint32_t)((int64_t)sh.m * sh.n * 2);
   p.ldq = sh.n;
   p.K = sh.m;
-  return launch<OP_APPLY, false, true, BM, BN, ANVIL_APPLY_WM, ANVIL_APPLY_WN, ANVIL_APPLY_STAGES>(p, sh.g, stream);
+  return launch<OP_APPLY, false, true, BM, BN, WM, WN, STAGES, BK, false>(p, sh.g, stream);
+}
+
+hipError_t launch_apply(const uint16_t* x, const uint16_t* bm, uint16_t* c, float coef_a,
+                        bool split, const Shape& sh, hipStream_t stream) {
+  const int64_t wide_tiles = (int64_t)ceil_div(sh.m, 128) * ceil_div(sh.n, 256) * sh.g;
+  if (wide_tiles >= kFullRound)
+    return launch_apply_cfg<128, 256, 2, 2, 3, 32>(x, bm, c, coef_a, split, sh, stream);
+  return launch_apply_cfg<128, 128, 2, 2, 2, 64>(x, bm, c, coef_a, split, sh, stream);
 }
 
 }  // namespace anvil

@@ -10,8 +10,8 @@
 //
 // HBM-bound: each element reads grad (4 B) and both rails (8 B) and writes both rails (8 B) and
 // x (2 B) — 22 bytes, touched once.  Each thread moves groups of 4 elements with 16-byte loads
-// and stores (8-byte for x); a grid-stride loop over a grid sized to a few waves per CU keeps
-// enough loads in flight.  grad is streamed with non-temporal loads (read once, never reused).
+// and stores (8-byte for x), several groups per iteration with all loads issued first; grad and
+// the rails stream through with non-temporal accesses, x stays cacheable for the Gram after it.
 #include "device_common.h"
 #include "launchers.h"
 
@@ -27,30 +27,53 @@ __device__ __forceinline__ float lerp_doc(float start, float end, float weight) 
   return start + weight * (end - start);
 }
 
+// Groups of 4 elements per thread per iteration, and workgroups per CU of the grid (grid-stride
+// beyond); chosen by measurement on MI355X (about 5.2 TB/s on the 24x2816x768 bank).
+constexpr int kUnroll = 4;
+constexpr int kBlocksPerCu = 16;
+
+// Each thread moves UNROLL groups of 4 elements per iteration: all loads first (3*UNROLL
+// 16-byte loads in flight), then the arithmetic, then the stores.  A block covers
+// UNROLL*256 consecutive groups, so every load and store instruction stays coalesced.
+template <int UNROLL>
 __global__ __launch_bounds__(256) void momentum_kernel(const f32x4_t* __restrict__ grad,
                                                        f32x4_t* __restrict__ v0,
                                                        f32x4_t* __restrict__ v1,
                                                        u32x2_t* __restrict__ x, int64_t n4,
                                                        RailWeights rw) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
-    const f32x4_t g = __builtin_nontemporal_load(grad + i);
-    f32x4_t a = v0[i];
-    f32x4_t b = v1[i];
-    float y[4];
+  const int64_t chunk = (int64_t)UNROLL * blockDim.x;
+  const int64_t stride = chunk * gridDim.x;
+  for (int64_t base = (int64_t)blockIdx.x * chunk + threadIdx.x; base < n4; base += stride) {
+    f32x4_t g[UNROLL], a[UNROLL], c[UNROLL];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      a[e] = lerp_doc(a[e], g[e], rw.wf);
-      b[e] = lerp_doc(b[e], g[e], rw.ws);
-      const float blend = rw.w * a[e] + rw.omw * b[e];
-      y[e] = lerp_doc(g[e], blend, rw.mu);
+    for (int u = 0; u < UNROLL; ++u) {
+      const int64_t i = base + (int64_t)u * blockDim.x;
+      if (i < n4) {
+        g[u] = __builtin_nontemporal_load(grad + i);
+        a[u] = v0[i];
+        c[u] = v1[i];
+      }
     }
-    v0[i] = a;
-    v1[i] = b;
-    u32x2_t packed;
-    packed[0] = pack_bf16x2(y[0], y[1]);
-    packed[1] = pack_bf16x2(y[2], y[3]);
-    x[i] = packed;
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int64_t i = base + (int64_t)u * blockDim.x;
+      if (i >= n4) continue;
+      float y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a[u][e] = lerp_doc(a[u][e], g[u][e], rw.wf);
+        c[u][e] = lerp_doc(c[u][e], g[u][e], rw.ws);
+        const float blend = rw.w * a[u][e] + rw.omw * c[u][e];
+        y[e] = lerp_doc(g[u][e], blend, rw.mu);
+      }
+      // the rails are next read one step later: stream them past the caches
+      __builtin_nontemporal_store(a[u], v0 + i);
+      __builtin_nontemporal_store(c[u], v1 + i);
+      u32x2_t packed;
+      packed[0] = pack_bf16x2(y[0], y[1]);
+      packed[1] = pack_bf16x2(y[2], y[3]);
+      x[i] = packed;   // read right away by the first Gram: keep it cacheable
+    }
   }
 }
 
@@ -67,11 +90,12 @@ hipError_t launch_momentum(const float* grad, float* v0, float* v1, uint16_t* x,
   rw.mu = momentum;
   const int64_t n4 = count / 4;
   const int threads = 256;
-  int64_t blocks = (n4 + threads - 1) / threads;
-  const int64_t max_blocks = 256 * 16;      // 16 workgroups per CU on 256 CUs, grid-stride beyond
+  int64_t blocks = (n4 + threads * kUnroll - 1) / (threads * kUnroll);
+  const int64_t max_blocks = 256 * kBlocksPerCu;
   if (blocks > max_blocks) blocks = max_blocks;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(momentum_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream,
+  hipLaunchKernelGGL(momentum_kernel<kUnroll>, dim3((unsigned)blocks), dim3(threads), 0,
+                     stream,
                      reinterpret_cast<const f32x4_t*>(grad), reinterpret_cast<f32x4_t*>(v0),
                      reinterpret_cast<f32x4_t*>(v1), reinterpret_cast<u32x2_t*>(x), n4, rw);
   return hipGetLastError();
