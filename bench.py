@@ -1,7 +1,7 @@
 """Benchmark of the ANVIL bank step on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload mlp|qk|vo|vs|us|single_wide] [--all]
-                    [--no-cpu-baseline] [--stages]
+                    [--no-cpu-baseline] [--copy-calibration BYTES]
 
 A step is one anvil_bank_step call over the whole stack (momentum, normalisation and the six
 Gram / polynomial / apply maps) on a gradient already resident in HBM.  The default workload is
@@ -45,6 +45,26 @@ def flops(g, m, n):
 
 def momentum_bytes(g, m, n):
     return 22 * g * m * n
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "apply_mlp_24x2816x768_traffic.md")
+GEMM_SOURCE = os.path.join(ROOT, "orthogonalizing_polynomial_cascade_amd", "csrc", "gemm.hip")
+
+
+def measured_apply_traffic():
+    """HBM bytes per apply launch on the mlp bank from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE scaled by a plain copy of known size), or None when the GEMM
+    source has changed since the counters were taken."""
+    import hashlib
+    try:
+        fields = dict(l.split(": ", 1) for l in open(TRAFFIC_PROFILE).read().splitlines()
+                      if l.startswith(("traffic_bytes_per_launch: ", "gemm_source_sha256_16: ")))
+        digest = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()[:16]
+    except OSError:
+        return None
+    if fields.get("gemm_source_sha256_16", "").strip() != digest:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
 
 
 def _events():
@@ -113,7 +133,7 @@ def time_stages(anvil, w, reps=20):
     return res
 
 
-def cpu_baseline(w, budget_s=20.0):
+def cpu_baseline(w, budget_s=15.0):
     """The oracle on a bounded sample of the same workload: whole bank steps of single matrices
     until about budget_s of CPU time, reported as matrices/s."""
     from oracle import anvil_oracle as O
@@ -130,7 +150,7 @@ def cpu_baseline(w, budget_s=20.0):
         O.bank_step(G, v, mu, fb, fw)
         done += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or done >= 8:
+        if el >= budget_s or done >= 64:
             break
     return {"value": done / el, "unit": "matrices/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{done} single-matrix bank steps ({w.m}x{w.n}, numpy fp64 products with "
@@ -166,6 +186,9 @@ def main():
     ap.add_argument("--workload", default="mlp")
     ap.add_argument("--all", action="store_true", help="also report every workload (stderr)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes three times (the reference "
+                         "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the ANVIL bank step has no cross-GPU path in this build "
@@ -177,6 +200,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        n = args.copy_calibration // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 4 * n, "launches": 3}), flush=True)
+        return
     anvil.load()
 
     w, rec = run_workload(anvil, args.workload, args.steps, args.warmup)
@@ -210,7 +242,10 @@ def main():
         "apply_tflops": rec["apply_tflops"],
         "roofline": {"bound": "mfma", "kernel": "apply (gemm_kernel<2>)", "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": None},
+                     "traffic": measured_apply_traffic() if w.name == "mlp" else None,
+                     "traffic_unit": "bytes per launch",
+                     "algorithmic_bytes": 2 * w.g * (2 * w.m * w.n + min(w.m, w.n) ** 2),
+                     "flops_per_launch": apply_flops},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
