@@ -257,3 +257,82 @@ def bank_step(grad, velocity, momentum, fast_beta, fast_weight, split: bool | No
     X = R(y)
     out = cascade(X, split=split)
     return bf16_bits(out), v
+
+
+# --------------------------------------------------------------------------------------------
+# The rest of the bank update: per-lane energy equalizer, sign-aligned decay with a
+# mantissa-tracked fp32 master (modded-nanogpt anvil.py, `_rail_equalizer`,
+# `_sign_aligned_decay_update`, `anvil_bank_update`)
+# --------------------------------------------------------------------------------------------
+
+def lane_axis(m: int, n: int) -> int:
+    """Axis the equalizer reduces over: the columns (axis -1) when rows >= cols, else the rows.
+
+    The page's docstring calls it the longer dimension, but its code sets the reduction axis to
+    the last one whenever rows >= cols; the code is followed.  The lanes are what remains: one per
+    row (rows >= cols) or one per column."""
+    return -1 if m >= n else -2
+
+
+def equalizer(v, lane_energy, beta2):
+    """Per-lane energy equalizer.
+
+    v: bf16 values (fp32 array) [g, m, n]; lane_energy: fp32 [g, m, 1] (rows >= cols) or
+    [g, 1, n].  Returns (equalized bf16 values, new lane_energy).  Steps, all fp32:
+      lane power  = mean of v^2 along the reduction axis (sum taken in fp64, rounded to fp32,
+                    then divided by the lane length);
+      pre norm    = sqrt(sum over lanes of lane power * lane length);
+      energy      = energy + (1 - beta2) * (power - energy)      (lerp; 1 - beta2 a host double);
+      gain        = 1 / sqrt(max(energy, 1e-10))                 (correctly rounded);
+      post norm   = sqrt(sum over lanes of (power * length) * gain^2);
+      scale       = gain * (pre norm / max(post norm, 1e-10));
+      v          <- bf16(v * bf16(scale)).
+    """
+    v = np.asarray(v, dtype=F32)
+    g, m, n = v.shape
+    ax = lane_axis(m, n)
+    length = n if ax == -1 else m
+    sq = v * v
+    power = (sq.astype(np.float64).sum(axis=ax, keepdims=True).astype(F32) / F32(length)).astype(F32)
+    psum = power.astype(np.float64).sum(axis=(-2, -1), keepdims=True).astype(F32)
+    pre = np.sqrt((psum * F32(length)).astype(F32)).astype(F32)
+    e = np.asarray(lane_energy, dtype=F32)
+    e = lerp(e, power, F32(1.0 - beta2)).astype(F32)
+    gain = (1.0 / np.sqrt(np.maximum(e, F32(1e-10)).astype(np.float64))).astype(F32)
+    post_power = ((power * F32(length)).astype(F32) * (gain * gain).astype(F32)).astype(F32)
+    post = np.sqrt(post_power.astype(np.float64).sum(axis=(-2, -1), keepdims=True).astype(F32)).astype(F32)
+    scale = (gain * (pre / np.maximum(post, F32(1e-10))).astype(F32)).astype(F32)
+    out = R(v * R(scale))
+    return out, e
+
+
+def decay_update(p_bits, mantissa, update, eff_wd, eff_lr, gate):
+    """Sign-aligned decay and parameter update on a bf16 parameter with a 16-bit mantissa.
+
+    The fp32 master is the parameter's bf16 bits (high half) joined with the mantissa (low half).
+    Decay applies where gate * master >= 0 (gate: the slow rail).  master <- (master -
+    ((master * aligned) * wd) * lr) - update * lr, each operation fp32; lr is per matrix.  The new
+    master splits back into its high half (the new bf16 parameter: a truncation) and low half.
+    Returns (new p_bits, new mantissa), both uint16.
+    """
+    raw = (np.asarray(p_bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)) | \
+        np.asarray(mantissa, dtype=np.uint16).astype(np.uint32)
+    p = raw.view(F32)
+    gate = np.asarray(gate, dtype=F32)
+    aligned = ((gate * p).astype(F32) >= 0).astype(F32)
+    lr = np.asarray(eff_lr, dtype=F32).reshape(-1, 1, 1)
+    t1 = (((p * aligned).astype(F32) * F32(eff_wd)).astype(F32) * lr).astype(F32)
+    t2 = (np.asarray(update, dtype=F32) * lr).astype(F32)
+    newp = ((p - t1).astype(F32) - t2).astype(F32)
+    raw2 = newp.view(np.uint32)
+    return (raw2 >> np.uint32(16)).astype(np.uint16), (raw2 & np.uint32(0xFFFF)).astype(np.uint16)
+
+
+def bank_update(grad, velocity, momentum, fast_beta, fast_weight, lane_energy, beta2, p_bits,
+                mantissa, eff_wd, eff_lr):
+    """The whole bank update: momentum and cascade, equalizer, sign-aligned decay (gate = the new
+    slow rail).  Returns (update bits, velocity, lane_energy, p_bits, mantissa)."""
+    out_bits, v = bank_step(grad, velocity, momentum, fast_beta, fast_weight)
+    upd, e = equalizer(bf16_to_f32(out_bits), lane_energy, beta2)
+    pb, mb = decay_update(p_bits, mantissa, upd, eff_wd, eff_lr, v[1])
+    return bf16_bits(upd), v, e, pb, mb
