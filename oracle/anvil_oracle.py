@@ -274,19 +274,18 @@ def lane_axis(m: int, n: int) -> int:
     return -1 if m >= n else -2
 
 
-def equalizer(v, lane_energy, beta2):
-    """Per-lane energy equalizer.
+def equalizer_terms(v, lane_energy, beta2):
+    """The per-lane terms of the equalizer: (lane power, new lane energy, bf16 lane scale).
 
     v: bf16 values (fp32 array) [g, m, n]; lane_energy: fp32 [g, m, 1] (rows >= cols) or
-    [g, 1, n].  Returns (equalized bf16 values, new lane_energy).  Steps, all fp32:
+    [g, 1, n]; every result has lane_energy's shape.  Steps, all fp32:
       lane power  = mean of v^2 along the reduction axis (sum taken in fp64, rounded to fp32,
                     then divided by the lane length);
       pre norm    = sqrt(sum over lanes of lane power * lane length);
       energy      = energy + (1 - beta2) * (power - energy)      (lerp; 1 - beta2 a host double);
       gain        = 1 / sqrt(max(energy, 1e-10))                 (correctly rounded);
       post norm   = sqrt(sum over lanes of (power * length) * gain^2);
-      scale       = gain * (pre norm / max(post norm, 1e-10));
-      v          <- bf16(v * bf16(scale)).
+      scale       = bf16(gain * (pre norm / max(post norm, 1e-10))).
     """
     v = np.asarray(v, dtype=F32)
     g, m, n = v.shape
@@ -302,8 +301,15 @@ def equalizer(v, lane_energy, beta2):
     post_power = ((power * F32(length)).astype(F32) * (gain * gain).astype(F32)).astype(F32)
     post = np.sqrt(post_power.astype(np.float64).sum(axis=(-2, -1), keepdims=True).astype(F32)).astype(F32)
     scale = (gain * (pre / np.maximum(post, F32(1e-10))).astype(F32)).astype(F32)
-    out = R(v * R(scale))
-    return out, e
+    return power, e, R(scale)
+
+
+def equalizer(v, lane_energy, beta2):
+    """Per-lane energy equalizer (the terms above), then v <- bf16(v * scale).
+
+    Returns (equalized bf16 values, new lane_energy)."""
+    _, e, scale = equalizer_terms(v, lane_energy, beta2)
+    return R(np.asarray(v, dtype=F32) * scale), e
 
 
 def decay_update(p_bits, mantissa, update, eff_wd, eff_lr, gate):
