@@ -90,7 +90,8 @@ int anvil_bank_step_ws(const float* grad, float* velocity, float momentum, float
                        float fast_weight, uint16_t* out, int64_t g, int64_t m, int64_t n,
                        void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes for a [g, m, n] bank step (0 for an empty stack, or for unsupported sizes). */
+/* Workspace bytes for a [g, m, n] bank step or bank update (0 for an empty stack, or for
+ * unsupported sizes). */
 size_t anvil_workspace_bytes(int64_t g, int64_t m, int64_t n);
 
 /* Frees every cached workspace on every device.  Synchronises each device first. */
@@ -133,6 +134,61 @@ int anvil_poly(const uint16_t* a, uint16_t* b_out, float coef_b, float coef_c, i
  * rounded to bf16 first and coef_a X is added to it in fp32.  c_out may not overlap x or b. */
 int anvil_apply(const uint16_t* x, const uint16_t* b, uint16_t* c_out, float coef_a, int split,
                 int64_t g, int64_t m, int64_t n, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * The rest of the bank update (anvil.py, `_rail_equalizer`, `_sign_aligned_decay_update`,
+ * `anvil_bank_update`).
+ *
+ * Equalizer lanes: one per row when m >= n (the equalizer reduces over the columns), else one
+ * per column (reducing over the rows); lanes = anvil_equalizer_lanes(m, n), lane length = the
+ * other dimension.  Per matrix, in fp32: power = mean over the lane of u^2; pre = sqrt(sum of
+ * power * length); energy += (1 - beta2) * (power - energy) (1 - beta2 formed in double, then
+ * taken as fp32); gain = 1/sqrt(max(energy, 1e-10)); post = sqrt(sum of (power * length) *
+ * gain^2); scale = bf16(gain * (pre / max(post, 1e-10))); u <- bf16(u * scale).
+ *
+ * Decay: the fp32 master is (param bits << 16) | mantissa; where gate * master >= 0 (gate: the
+ * slow rail) it decays: master <- (master - ((master * aligned) * eff_wd) * eff_lr[matrix]) -
+ * u * eff_lr[matrix]; the new param bits are its high half (truncation), the mantissa its low
+ * half.
+ * ------------------------------------------------------------------------------------------ */
+
+/* One whole bank update: anvil_bank_step into `update`, then the equalizer (update rewritten in
+ * place with the equalized values, lane_energy updated in place), then the decay of
+ * (param, mantissa) gated on the slow rail this call has just written.
+ *   update       bf16 [g,m,n] out (also the cascade's ping-pong buffer)
+ *   lane_energy  fp32 [g, lanes] in/out (the page's [g,m,1] or [g,1,n])
+ *   beta2        the energy EMA's decay, a double (a Python float on the page); the lerp
+ *                weight is fp32(1 - beta2) with the subtraction in double
+ *   param        bf16 bits [g,m,n] in/out; mantissa uint16 [g,m,n] in/out
+ *   eff_wd       decay factor (wd_mul * weight_decay * lr on the page); eff_lr fp32 [g] device
+ * No two of grad, velocity, update, lane_energy, param, mantissa, eff_lr may overlap.  Uses the
+ * cached workspace (anvil_workspace_bytes covers it). */
+int anvil_bank_update(const float* grad, float* velocity, float momentum, float fast_beta,
+                      float fast_weight, uint16_t* update, float* lane_energy, double beta2,
+                      uint16_t* param, uint16_t* mantissa, float eff_wd, const float* eff_lr,
+                      int64_t g, int64_t m, int64_t n, void* stream);
+
+/* As anvil_bank_update with a caller-owned workspace (anvil_workspace_bytes(g, m, n) bytes,
+ * 256-byte aligned); allocates nothing. */
+int anvil_bank_update_ws(const float* grad, float* velocity, float momentum, float fast_beta,
+                         float fast_weight, uint16_t* update, float* lane_energy, double beta2,
+                         uint16_t* param, uint16_t* mantissa, float eff_wd, const float* eff_lr,
+                         int64_t g, int64_t m, int64_t n, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Equalizer lanes per matrix for shape m x n (0 for unsupported shapes). */
+int64_t anvil_equalizer_lanes(int64_t m, int64_t n);
+
+/* The equalizer alone: update bf16 [g,m,n] rescaled IN PLACE, lane_energy fp32 [g, lanes]
+ * updated in place; lane_scratch fp32 [2*g*lanes] is overwritten (lane powers and scales). */
+int anvil_equalize(uint16_t* update, float* lane_energy, double beta2, float* lane_scratch,
+                   int64_t g, int64_t m, int64_t n, void* stream);
+
+/* The decay alone: (param, mantissa) updated in place from update bf16 [g,m,n] read only, gate
+ * fp32 [g,m,n] read only, eff_lr fp32 [g]. */
+int anvil_decay_update(uint16_t* param, uint16_t* mantissa, const uint16_t* update, float eff_wd,
+                       const float* eff_lr, const float* gate, int64_t g, int64_t m, int64_t n,
+                       void* stream);
 
 #ifdef __cplusplus
 }

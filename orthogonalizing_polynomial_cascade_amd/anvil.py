@@ -23,6 +23,7 @@ ANVIL_ERR_HIP = 6
 
 # Every symbol include/anvil.h declares, with its ctypes signature (restype, argtypes).
 _vp, _i64, _f, _i, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_size_t
+_d = ctypes.c_double
 SIGNATURES = {
     "anvil_status_string": (ctypes.c_char_p, [_i]),
     "anvil_last_hip_error": (_i, []),
@@ -37,6 +38,13 @@ SIGNATURES = {
     "anvil_normalize": (_i, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "anvil_poly": (_i, [_vp, _vp, _f, _f, _i64, _i64, _vp]),
     "anvil_apply": (_i, [_vp, _vp, _vp, _f, _i, _i64, _i64, _i64, _vp]),
+    "anvil_bank_update": (_i, [_vp, _vp, _f, _f, _f, _vp, _vp, _d, _vp, _vp, _f, _vp,
+                               _i64, _i64, _i64, _vp]),
+    "anvil_bank_update_ws": (_i, [_vp, _vp, _f, _f, _f, _vp, _vp, _d, _vp, _vp, _f, _vp,
+                                  _i64, _i64, _i64, _vp, _sz, _vp]),
+    "anvil_equalizer_lanes": (_i64, [_i64, _i64]),
+    "anvil_equalize": (_i, [_vp, _vp, _d, _vp, _i64, _i64, _i64, _vp]),
+    "anvil_decay_update": (_i, [_vp, _vp, _vp, _f, _vp, _vp, _i64, _i64, _i64, _vp]),
 }
 
 _lib = None
@@ -223,6 +231,81 @@ def anvil_apply(x, b, coef_a, split, c_out=None, stream=None):
     _check("anvil_apply", lib.anvil_apply(_ptr(x), _ptr(b), _ptr(c_out), coef_a, int(bool(split)),
                                           g, m, n, _stream(stream)))
     return c_out
+
+
+def equalizer_lanes(m: int, n: int) -> int:
+    return int(load().anvil_equalizer_lanes(m, n))
+
+
+def anvil_bank_update(grad, velocity, momentum, fast_beta, fast_weight, lane_energy, beta2,
+                      param, mantissa, eff_wd, eff_lr, update=None, workspace=None, stream=None):
+    """One whole bank update (step, equalizer, sign-aligned decay).
+
+    grad fp32 [g,m,n]; velocity fp32 [2,g,m,n], lane_energy fp32 [g, lanes], param bf16 [g,m,n]
+    and mantissa int16/uint16 [g,m,n] are updated in place; eff_lr fp32 [g].  Returns the
+    equalized bf16 update."""
+    import torch
+    lib = load()
+    _need(grad, "grad", torch.float32)
+    g, m, n = _gmn(grad)
+    _need(velocity, "velocity", torch.float32, (2, g, m, n))
+    _need(lane_energy, "lane_energy", torch.float32)
+    if lane_energy.numel() != g * equalizer_lanes(m, n):
+        raise ValueError("lane_energy must hold g * lanes values")
+    _need(param, "param", torch.bfloat16, (g, m, n))
+    if mantissa.dtype not in (torch.int16, torch.uint16):
+        raise TypeError("mantissa must be a 16-bit integer tensor")
+    _need(mantissa, "mantissa", mantissa.dtype, (g, m, n))
+    _need(eff_lr, "eff_lr", torch.float32, (g,))
+    if update is None:
+        update = torch.empty((g, m, n), dtype=torch.bfloat16, device=grad.device)
+    _need(update, "update", torch.bfloat16, (g, m, n))
+    args = [_ptr(grad), _ptr(velocity), momentum, fast_beta, fast_weight, _ptr(update),
+            _ptr(lane_energy), beta2, _ptr(param), _ptr(mantissa), eff_wd, _ptr(eff_lr), g, m, n]
+    if workspace is None:
+        _check("anvil_bank_update", lib.anvil_bank_update(*args, _stream(stream)))
+    else:
+        _need(workspace, "workspace", torch.uint8)
+        _check("anvil_bank_update_ws", lib.anvil_bank_update_ws(*args, _ptr(workspace),
+                                                                workspace.numel(), _stream(stream)))
+    return update
+
+
+def anvil_equalize(update, lane_energy, beta2, lane_scratch=None, stream=None):
+    """In-place equalizer on a bf16 [g,m,n] update; lane_energy fp32 [g, lanes] in place."""
+    import torch
+    lib = load()
+    _need(update, "update", torch.bfloat16)
+    g, m, n = _gmn(update)
+    lanes = equalizer_lanes(m, n)
+    _need(lane_energy, "lane_energy", torch.float32)
+    if lane_energy.numel() != g * lanes:
+        raise ValueError("lane_energy must hold g * lanes values")
+    if lane_scratch is None:
+        lane_scratch = torch.empty(2 * g * lanes, dtype=torch.float32, device=update.device)
+    _need(lane_scratch, "lane_scratch", torch.float32)
+    if lane_scratch.numel() < 2 * g * lanes:
+        raise ValueError("lane_scratch must hold 2 * g * lanes values")
+    _check("anvil_equalize", lib.anvil_equalize(_ptr(update), _ptr(lane_energy), beta2,
+                                                _ptr(lane_scratch), g, m, n, _stream(stream)))
+    return update
+
+
+def anvil_decay_update(param, mantissa, update, eff_wd, eff_lr, gate, stream=None):
+    """In-place sign-aligned decay of (param bf16, mantissa uint16) by the bf16 update."""
+    import torch
+    lib = load()
+    _need(param, "param", torch.bfloat16)
+    g, m, n = _gmn(param)
+    if mantissa.dtype not in (torch.int16, torch.uint16):
+        raise TypeError("mantissa must be a 16-bit integer tensor")
+    _need(mantissa, "mantissa", mantissa.dtype, (g, m, n))
+    _need(update, "update", torch.bfloat16, (g, m, n))
+    _need(eff_lr, "eff_lr", torch.float32, (g,))
+    _need(gate, "gate", torch.float32, (g, m, n))
+    _check("anvil_decay_update", lib.anvil_decay_update(_ptr(param), _ptr(mantissa), _ptr(update),
+                                                        eff_wd, _ptr(eff_lr), _ptr(gate), g, m, n,
+                                                        _stream(stream)))
 
 
 def rail_scalars(step: int):

@@ -16,7 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libanvil.so")
-SOURCES = ["momentum.hip", "gemm.hip", "normalize.hip", "api.hip"]
+SOURCES = ["momentum.hip", "gemm.hip", "normalize.hip", "update.hip", "api.hip"]
 ARCH = "gfx950"
 
 

@@ -63,7 +63,7 @@ size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // Workspace regions: ping-pong X (bf16 [g,m,n]), A and B (bf16 [g,s,s]), trace partials
 // (fp32 [g, slots]) and d (fp32 [g]).
 struct Layout {
-  size_t ping, a, b, partials, d, total;
+  size_t ping, a, b, partials, d, lanes, total;
 };
 
 Layout layout_for(const Shape& sh) {
@@ -81,6 +81,8 @@ Layout layout_for(const Shape& sh) {
   off += round_up(g * anvil::gram_trace_slots(sh.s()) * 4);
   l.d = off;
   off += round_up(g * 4);
+  l.lanes = off;   // equalizer scratch: lane powers and lane scales
+  off += round_up(2 * g * anvil::equalizer_lanes(sh) * 4);
   l.total = off;
   return l;
 }
@@ -133,9 +135,85 @@ int run_step(const float* grad, float* velocity, float momentum, float fast_beta
   return ANVIL_OK;
 }
 
+int check_update_args(const float* grad, const float* velocity, const uint16_t* update,
+                      const float* lane_energy, const uint16_t* param, const uint16_t* mantissa,
+                      const float* eff_lr, const Shape& sh) {
+  if (!lane_energy || !param || !mantissa || !eff_lr) return ANVIL_ERR_INVALID_ARG;
+  if (!aligned(param, 16) || !aligned(mantissa, 16) || !aligned(lane_energy, 4) ||
+      !aligned(eff_lr, 4))
+    return ANVIL_ERR_MISALIGNED;
+  const size_t cnt = static_cast<size_t>(sh.g) * sh.m * sh.n;
+  const size_t lb = static_cast<size_t>(sh.g) * anvil::equalizer_lanes(sh) * 4;
+  const void* bufs[6] = {grad, velocity, update, param, mantissa, lane_energy};
+  const size_t sizes[6] = {cnt * 4, cnt * 8, cnt * 2, cnt * 2, cnt * 2, lb};
+  for (int i = 0; i < 6; ++i)
+    for (int j = i + 1; j < 6; ++j)
+      if (bufs[i] && bufs[j] && overlap(bufs[i], sizes[i], bufs[j], sizes[j])) return ANVIL_ERR_ALIAS;
+  if (overlap(eff_lr, sh.g * 4, param, cnt * 2) || overlap(eff_lr, sh.g * 4, mantissa, cnt * 2) ||
+      overlap(eff_lr, sh.g * 4, lane_energy, lb))
+    return ANVIL_ERR_ALIAS;
+  return ANVIL_OK;
+}
+
+// The whole bank update: the step (into `update`), then the equalizer and the decay, gated on the
+// slow rail the step has just written.
+int run_update(const float* grad, float* velocity, float momentum, float fast_beta,
+               float fast_weight, uint16_t* update, float* lane_energy, double beta2,
+               uint16_t* param, uint16_t* mantissa, float eff_wd, const float* eff_lr,
+               const Shape& sh, char* ws, hipStream_t stream) {
+  int st = run_step(grad, velocity, momentum, fast_beta, fast_weight, update, sh, ws, stream);
+  if (st != ANVIL_OK) return st;
+  const Layout l = layout_for(sh);
+  const int64_t count = sh.g * sh.m * sh.n;
+  return hip_status(anvil::launch_equalize(update, lane_energy, beta2,
+                                           reinterpret_cast<float*>(ws + l.lanes), sh, stream,
+                                           param, mantissa, velocity + count, eff_lr, eff_wd));
+}
+
 // Workspace cache of the allocating entry point, one grow-only buffer per (device, stream).
 std::mutex g_ws_mutex;
 std::map<std::pair<int, hipStream_t>, std::pair<void*, size_t>> g_ws;
+
+// The cached workspace of at least `need` bytes for the current device and `stream`.
+int cached_workspace(size_t need, hipStream_t hs, char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  auto& slot = g_ws[{dev, hs}];
+  if (slot.second < need) {
+    if (slot.first) {
+      // the old buffer may still be in use by work queued on this stream
+      e = hipStreamSynchronize(hs);
+      if (e != hipSuccess) return hip_status(e);
+      e = hipFree(slot.first);
+      slot = {nullptr, 0};
+      if (e != hipSuccess) return hip_status(e);
+    }
+    void* p = nullptr;
+    if (hipMalloc(&p, need) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return ANVIL_ERR_OOM;
+    }
+    slot = {p, need};
+  }
+  *out = static_cast<char*>(slot.first);
+  return ANVIL_OK;
+}
+
+// Checks of a caller-owned workspace against the step's buffers.
+int check_workspace(const void* workspace, size_t workspace_bytes, const float* grad,
+                    const float* velocity, const uint16_t* out, const Shape& sh) {
+  if (!workspace) return ANVIL_ERR_INVALID_ARG;
+  if (!aligned(workspace, kAlign)) return ANVIL_ERR_MISALIGNED;
+  const Layout l = layout_for(sh);
+  if (workspace_bytes < l.total) return ANVIL_ERR_UNSUPPORTED;
+  const size_t cnt = static_cast<size_t>(sh.g) * sh.m * sh.n;
+  if (overlap(workspace, l.total, grad, cnt * 4) || overlap(workspace, l.total, velocity, cnt * 8) ||
+      overlap(workspace, l.total, out, cnt * 2))
+    return ANVIL_ERR_ALIAS;
+  return ANVIL_OK;
+}
 
 }  // namespace
 
@@ -175,14 +253,8 @@ int anvil_bank_step_ws(const float* grad, float* velocity, float momentum, float
   if (st != ANVIL_OK || empty) return st;
   st = check_step_args(grad, velocity, out, sh);
   if (st != ANVIL_OK) return st;
-  if (!workspace) return ANVIL_ERR_INVALID_ARG;
-  if (!aligned(workspace, kAlign)) return ANVIL_ERR_MISALIGNED;
-  const Layout l = layout_for(sh);
-  if (workspace_bytes < l.total) return ANVIL_ERR_UNSUPPORTED;
-  const size_t cnt = static_cast<size_t>(sh.g) * sh.m * sh.n;
-  if (overlap(workspace, l.total, grad, cnt * 4) || overlap(workspace, l.total, velocity, cnt * 8) ||
-      overlap(workspace, l.total, out, cnt * 2))
-    return ANVIL_ERR_ALIAS;
+  st = check_workspace(workspace, workspace_bytes, grad, velocity, out, sh);
+  if (st != ANVIL_OK) return st;
   return run_step(grad, velocity, momentum, fast_beta, fast_weight, out, sh,
                   static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
 }
@@ -196,35 +268,106 @@ int anvil_bank_step(const float* grad, float* velocity, float momentum, float fa
   if (st != ANVIL_OK || empty) return st;
   st = check_step_args(grad, velocity, out, sh);
   if (st != ANVIL_OK) return st;
-  const size_t need = layout_for(sh).total;
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_status(e);
-  void* ws = nullptr;
-  {
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
-    auto& slot = g_ws[{dev, hs}];
-    if (slot.second < need) {
-      if (slot.first) {
-        // the old buffer may still be in use by work queued on this stream
-        e = hipStreamSynchronize(hs);
-        if (e != hipSuccess) return hip_status(e);
-        e = hipFree(slot.first);
-        slot = {nullptr, 0};
-        if (e != hipSuccess) return hip_status(e);
-      }
-      void* p = nullptr;
-      if (hipMalloc(&p, need) != hipSuccess || !p) {
-        (void)hipGetLastError();
-        return ANVIL_ERR_OOM;
-      }
-      slot = {p, need};
-    }
-    ws = slot.first;
-  }
-  return run_step(grad, velocity, momentum, fast_beta, fast_weight, out, sh,
-                  static_cast<char*>(ws), hs);
+  char* ws = nullptr;
+  st = cached_workspace(layout_for(sh).total, hs, &ws);
+  if (st != ANVIL_OK) return st;
+  return run_step(grad, velocity, momentum, fast_beta, fast_weight, out, sh, ws, hs);
+}
+
+int anvil_bank_update(const float* grad, float* velocity, float momentum, float fast_beta,
+                      float fast_weight, uint16_t* update, float* lane_energy, double beta2,
+                      uint16_t* param, uint16_t* mantissa, float eff_wd, const float* eff_lr,
+                      int64_t g, int64_t m, int64_t n, void* stream) {
+  Shape sh;
+  bool empty = false;
+  int st = check_shape(g, m, n, &sh, &empty);
+  if (st != ANVIL_OK || empty) return st;
+  st = check_step_args(grad, velocity, update, sh);
+  if (st != ANVIL_OK) return st;
+  st = check_update_args(grad, velocity, update, lane_energy, param, mantissa, eff_lr, sh);
+  if (st != ANVIL_OK) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  char* ws = nullptr;
+  st = cached_workspace(layout_for(sh).total, hs, &ws);
+  if (st != ANVIL_OK) return st;
+  return run_update(grad, velocity, momentum, fast_beta, fast_weight, update, lane_energy, beta2,
+                    param, mantissa, eff_wd, eff_lr, sh, ws, hs);
+}
+
+int anvil_bank_update_ws(const float* grad, float* velocity, float momentum, float fast_beta,
+                         float fast_weight, uint16_t* update, float* lane_energy, double beta2,
+                         uint16_t* param, uint16_t* mantissa, float eff_wd, const float* eff_lr,
+                         int64_t g, int64_t m, int64_t n, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  Shape sh;
+  bool empty = false;
+  int st = check_shape(g, m, n, &sh, &empty);
+  if (st != ANVIL_OK || empty) return st;
+  st = check_step_args(grad, velocity, update, sh);
+  if (st != ANVIL_OK) return st;
+  st = check_update_args(grad, velocity, update, lane_energy, param, mantissa, eff_lr, sh);
+  if (st != ANVIL_OK) return st;
+  st = check_workspace(workspace, workspace_bytes, grad, velocity, update, sh);
+  if (st != ANVIL_OK) return st;
+  const Layout l = layout_for(sh);
+  const size_t cnt = static_cast<size_t>(sh.g) * sh.m * sh.n;
+  const size_t lb = static_cast<size_t>(sh.g) * anvil::equalizer_lanes(sh) * 4;
+  if (overlap(workspace, l.total, param, cnt * 2) || overlap(workspace, l.total, mantissa, cnt * 2) ||
+      overlap(workspace, l.total, lane_energy, lb) || overlap(workspace, l.total, eff_lr, sh.g * 4))
+    return ANVIL_ERR_ALIAS;
+  return run_update(grad, velocity, momentum, fast_beta, fast_weight, update, lane_energy, beta2,
+                    param, mantissa, eff_wd, eff_lr, sh, static_cast<char*>(workspace),
+                    static_cast<hipStream_t>(stream));
+}
+
+int64_t anvil_equalizer_lanes(int64_t m, int64_t n) {
+  Shape sh;
+  bool empty = false;
+  if (check_shape(1, m, n, &sh, &empty) != ANVIL_OK || empty) return 0;
+  return anvil::equalizer_lanes(sh);
+}
+
+int anvil_equalize(uint16_t* update, float* lane_energy, double beta2, float* lane_scratch,
+                   int64_t g, int64_t m, int64_t n, void* stream) {
+  Shape sh;
+  bool empty = false;
+  int st = check_shape(g, m, n, &sh, &empty);
+  if (st != ANVIL_OK || empty) return st;
+  if (!update || !lane_energy || !lane_scratch) return ANVIL_ERR_INVALID_ARG;
+  if (!aligned(update, 16) || !aligned(lane_energy, 4) || !aligned(lane_scratch, 4))
+    return ANVIL_ERR_MISALIGNED;
+  const size_t cnt = static_cast<size_t>(sh.g) * sh.m * sh.n;
+  const size_t lb = static_cast<size_t>(sh.g) * anvil::equalizer_lanes(sh) * 4;
+  if (overlap(update, cnt * 2, lane_energy, lb) || overlap(update, cnt * 2, lane_scratch, 2 * lb) ||
+      overlap(lane_energy, lb, lane_scratch, 2 * lb))
+    return ANVIL_ERR_ALIAS;
+  return hip_status(anvil::launch_equalize(update, lane_energy, beta2, lane_scratch, sh,
+                                           static_cast<hipStream_t>(stream), nullptr, nullptr,
+                                           nullptr, nullptr, 0.0f));
+}
+
+int anvil_decay_update(uint16_t* param, uint16_t* mantissa, const uint16_t* update, float eff_wd,
+                       const float* eff_lr, const float* gate, int64_t g, int64_t m, int64_t n,
+                       void* stream) {
+  Shape sh;
+  bool empty = false;
+  int st = check_shape(g, m, n, &sh, &empty);
+  if (st != ANVIL_OK || empty) return st;
+  if (!param || !mantissa || !update || !eff_lr || !gate) return ANVIL_ERR_INVALID_ARG;
+  if (!aligned(param, 16) || !aligned(mantissa, 16) || !aligned(update, 16) || !aligned(gate, 16) ||
+      !aligned(eff_lr, 4))
+    return ANVIL_ERR_MISALIGNED;
+  const size_t cnt = static_cast<size_t>(sh.g) * sh.m * sh.n;
+  const void* bufs[4] = {param, mantissa, update, gate};
+  const size_t sizes[4] = {cnt * 2, cnt * 2, cnt * 2, cnt * 4};
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(bufs[i], sizes[i], bufs[j], sizes[j])) return ANVIL_ERR_ALIAS;
+  if (overlap(eff_lr, sh.g * 4, param, cnt * 2) || overlap(eff_lr, sh.g * 4, mantissa, cnt * 2))
+    return ANVIL_ERR_ALIAS;
+  return hip_status(anvil::launch_decay(param, mantissa, update, eff_wd, eff_lr, gate, sh,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 int anvil_release_workspaces(void) {

@@ -32,4 +32,18 @@ hipError_t launch_poly(const uint16_t* a, uint16_t* b, float coef_b, float coef_
 hipError_t launch_apply(const uint16_t* x, const uint16_t* b, uint16_t* c, float coef_a,
                         bool split, const Shape& sh, hipStream_t stream);
 
+// Equalizer lanes of an m x n matrix: rows when m >= n, else columns.
+int equalizer_lanes(const Shape& sh);
+
+// Equalizer on u (in place) with lane energies updated in place; scratch holds 2*g*lanes fp32.
+// If param is not null, the same elementwise pass applies the sign-aligned decay to
+// (param, mantissa) with the rescaled u, gate (the slow rail), per-matrix lr and wd.
+hipError_t launch_equalize(uint16_t* u, float* lane_energy, double beta2, float* scratch,
+                           const Shape& sh, hipStream_t stream, uint16_t* param,
+                           uint16_t* mantissa, const float* gate, const float* lr, float wd);
+
+// The sign-aligned decay alone, with u as given.
+hipError_t launch_decay(uint16_t* param, uint16_t* mantissa, const uint16_t* u, float wd,
+                        const float* lr, const float* gate, const Shape& sh, hipStream_t stream);
+
 }  // namespace anvil

@@ -1,0 +1,281 @@
+// The rest of the bank update after the cascade: the per-lane energy equalizer and the
+// sign-aligned decay of a bf16 parameter with a 16-bit mantissa.
+//
+// Source: modded-nanogpt anvil.py, `_rail_equalizer`, `_sign_aligned_decay_update` and
+// `anvil_bank_update`.
+//
+// Lanes: one per row when rows >= cols (the equalizer reduces over the columns), else one per
+// column (reducing over the rows) -- the page's code, whose docstring calls the reduced axis the
+// longer one.  Per matrix, in fp32:
+//   power[l] = mean over the lane of u^2             pre  = sqrt(sum_l power[l] * len)
+//   e[l]    += (1 - beta2) * (power[l] - e[l])        gain = 1 / sqrt(max(e[l], 1e-10))
+//   post     = sqrt(sum_l (power[l] * len) * gain^2)  scale[l] = bf16(gain * (pre / max(post, 1e-10)))
+//   u       <- bf16(u * scale[lane])
+// then, per element, with the fp32 master m = (param bits << 16) | mantissa:
+//   m <- (m - ((m * [gate * m >= 0]) * wd) * lr[matrix]) - u * lr[matrix]
+//   param bits = high half of m (truncation), mantissa = low half.
+//
+// Three kernels: lane powers (deterministic fixed-order reductions), one workgroup per matrix for
+// the scales and the energy EMA, and one fused elementwise pass that rescales the update, writes
+// it back and applies the decay (HBM-bound: 16 bytes per element with the decay).
+#include "device_common.h"
+#include "launchers.h"
+
+namespace anvil {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float sqrt_rn(float x) {
+  // correctly rounded fp32 square root (fp64 root, then one rounding; 53 >= 2*24 + 2)
+  return static_cast<float>(__builtin_sqrt(static_cast<double>(x)));
+}
+
+__device__ __forceinline__ float rsqrt_rn(float x) {
+  // fp32 of 1/sqrt(x), from fp64
+  return static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(x)));
+}
+
+// Row lanes (rows >= cols): one wave per row, 8 elements per lane per step, butterfly sum.
+__global__ __launch_bounds__(kThreads) void lane_power_rows(const uint16_t* __restrict__ u,
+                                                            float* __restrict__ power, int m,
+                                                            int n) {
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * (kThreads / 64) + wave;
+  const int64_t b = blockIdx.y;
+  if (row >= m) return;
+  const uint16_t* r = u + (b * m + row) * (int64_t)n;
+  float s = 0.0f;
+  for (int c = lane * 8; c < n; c += 64 * 8) {
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(r + c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float lo = bf16_to_f32(v[e] & 0xFFFFu);
+      const float hi = bf16_to_f32(v[e] >> 16);
+      const float slo = lo * lo;
+      const float shi = hi * hi;
+      s += slo;
+      s += shi;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+  if (lane == 0) power[b * m + row] = s / static_cast<float>(n);
+}
+
+// Column lanes (rows < cols): a block covers 256 columns (32 chunks of 8) and 8 row groups; each
+// thread sums every 8th row of its chunk, then the row groups are added in order through LDS.
+__global__ __launch_bounds__(kThreads) void lane_power_cols(const uint16_t* __restrict__ u,
+                                                            float* __restrict__ power, int m,
+                                                            int n) {
+  __shared__ float part[8][257];
+  const int chunk = threadIdx.x & 31;
+  const int rg = threadIdx.x >> 5;
+  const int col0 = blockIdx.x * 256 + chunk * 8;
+  const int64_t b = blockIdx.y;
+  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (col0 < n) {
+    const uint16_t* base = u + b * (int64_t)m * n + col0;
+    for (int row = rg; row < m; row += 8) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(base + (int64_t)row * n);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = bf16_to_f32(v[e] & 0xFFFFu);
+        const float hi = bf16_to_f32(v[e] >> 16);
+        const float slo = lo * lo;
+        const float shi = hi * hi;
+        s[2 * e] += slo;
+        s[2 * e + 1] += shi;
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[rg][chunk * 8 + e] = s[e];
+  __syncthreads();
+  const int col = blockIdx.x * 256 + threadIdx.x;
+  if (col < n) {
+    float t = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) t += part[g][threadIdx.x];
+    power[b * n + col] = t / static_cast<float>(m);
+  }
+}
+
+// Fixed-order block sum of one value per thread (256 threads).
+__device__ float block_sum(float v, float* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  float t = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) t += red[w];
+  __syncthreads();
+  return t;
+}
+
+// One workgroup per matrix: pre and post norms, the energy EMA, the bf16 lane scales.
+__global__ __launch_bounds__(kThreads) void lane_scales(const float* __restrict__ power,
+                                                        float* __restrict__ energy,
+                                                        float* __restrict__ scale, int lanes,
+                                                        int len, float w_ema) {
+  __shared__ float red[kThreads / 64];
+  const int64_t b = blockIdx.x;
+  const float* pw = power + b * lanes;
+  float* en = energy + b * lanes;
+  float* sc = scale + b * lanes;
+  const float flen = static_cast<float>(len);
+
+  float ps = 0.0f;
+  for (int l = threadIdx.x; l < lanes; l += kThreads) ps += pw[l];
+  const float psum = block_sum(ps, red);
+  const float pre = sqrt_rn(psum * flen);
+
+  float qs = 0.0f;
+  for (int l = threadIdx.x; l < lanes; l += kThreads) {
+    const float p = pw[l];
+    const float e = en[l] + w_ema * (p - en[l]);
+    en[l] = e;
+    const float gain = rsqrt_rn(fmaxf(e, 1e-10f));
+    const float pl = p * flen;
+    const float g2 = gain * gain;
+    qs += pl * g2;
+    sc[l] = gain;   // the gain for now; the scale once the post norm is known
+  }
+  const float post = sqrt_rn(block_sum(qs, red));
+  const float ratio = pre / fmaxf(post, 1e-10f);
+  for (int l = threadIdx.x; l < lanes; l += kThreads) {
+    sc[l] = bf16_to_f32(f32_to_bf16(sc[l] * ratio));
+  }
+}
+
+struct DecayArgs {
+  uint16_t* param;        // nullptr: no decay
+  uint16_t* mantissa;
+  const float* gate;      // the slow rail
+  const float* lr;        // per matrix
+  float wd;
+};
+
+// Elementwise: u <- bf16(u * scale[lane]) (if scale), write u back (if write_u), then the decay
+// (if d.param).  8 elements per thread per step.
+__global__ __launch_bounds__(kThreads) void scale_decay(uint16_t* __restrict__ u,
+                                                        const float* __restrict__ scale,
+                                                        bool write_u, DecayArgs d, int m, int n,
+                                                        bool row_lanes, int64_t chunks_per_matrix,
+                                                        int64_t g) {
+  const int64_t total = chunks_per_matrix * g;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total; c += stride) {
+    const int64_t b = c / chunks_per_matrix;
+    const int64_t within = (c - b * chunks_per_matrix) * 8;
+    const int row = static_cast<int>(within / n);
+    const int col = static_cast<int>(within - (int64_t)row * n);
+    const int64_t off = c * 8;
+    u32x4_t uv = *reinterpret_cast<const u32x4_t*>(u + off);
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = bf16_to_f32(uv[e] & 0xFFFFu);
+      x[2 * e + 1] = bf16_to_f32(uv[e] >> 16);
+    }
+    if (scale != nullptr) {
+      const float* sb = scale + b * (row_lanes ? m : n);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float s = row_lanes ? sb[row] : sb[col + e];
+        x[e] = bf16_to_f32(f32_to_bf16(x[e] * s));
+      }
+      if (write_u) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) uv[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
+        *reinterpret_cast<u32x4_t*>(u + off) = uv;
+      }
+    }
+    if (d.param != nullptr) {
+      const u32x4_t pv = *reinterpret_cast<const u32x4_t*>(d.param + off);
+      const u32x4_t mv = *reinterpret_cast<const u32x4_t*>(d.mantissa + off);
+      const f32x4_t g0 = *reinterpret_cast<const f32x4_t*>(d.gate + off);
+      const f32x4_t g1 = *reinterpret_cast<const f32x4_t*>(d.gate + off + 4);
+      const float gate[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+      const float lr = d.lr[b];
+      u32x4_t po, mo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t pb = (e & 1) ? (pv[e >> 1] >> 16) : (pv[e >> 1] & 0xFFFFu);
+        const uint32_t mb = (e & 1) ? (mv[e >> 1] >> 16) : (mv[e >> 1] & 0xFFFFu);
+        const float master = __uint_as_float((pb << 16) | mb);
+        const float aligned = (gate[e] * master >= 0.0f) ? 1.0f : 0.0f;
+        const float t1 = ((master * aligned) * d.wd) * lr;
+        const float t2 = x[e] * lr;
+        const uint32_t raw = __float_as_uint((master - t1) - t2);
+        const uint32_t hi = raw >> 16;
+        const uint32_t lo = raw & 0xFFFFu;
+        if (e & 1) {
+          po[e >> 1] |= hi << 16;
+          mo[e >> 1] |= lo << 16;
+        } else {
+          po[e >> 1] = hi;
+          mo[e >> 1] = lo;
+        }
+      }
+      *reinterpret_cast<u32x4_t*>(d.param + off) = po;
+      *reinterpret_cast<u32x4_t*>(d.mantissa + off) = mo;
+    }
+  }
+}
+
+int64_t elementwise_blocks(int64_t chunks) {
+  int64_t blocks = (chunks + kThreads - 1) / kThreads;
+  const int64_t cap = 256 * 16;
+  return blocks < 1 ? 1 : (blocks > cap ? cap : blocks);
+}
+
+}  // namespace
+
+int equalizer_lanes(const Shape& sh) { return sh.m >= sh.n ? sh.m : sh.n; }
+
+hipError_t launch_equalize(uint16_t* u, float* lane_energy, double beta2, float* scratch,
+                           const Shape& sh, hipStream_t stream, uint16_t* param,
+                           uint16_t* mantissa, const float* gate, const float* lr, float wd) {
+  const bool rows = sh.m >= sh.n;
+  const int lanes = equalizer_lanes(sh);
+  const int len = rows ? sh.n : sh.m;
+  float* power = scratch;
+  float* scale = scratch + sh.g * lanes;
+  if (rows) {
+    hipLaunchKernelGGL(lane_power_rows, dim3((unsigned)((sh.m + 3) / 4), (unsigned)sh.g),
+                       dim3(kThreads), 0, stream, u, power, sh.m, sh.n);
+  } else {
+    hipLaunchKernelGGL(lane_power_cols, dim3((unsigned)((sh.n + 255) / 256), (unsigned)sh.g),
+                       dim3(kThreads), 0, stream, u, power, sh.m, sh.n);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // 1 - beta2 formed in double and taken as fp32, as the page's lerp weight
+  const float w_ema = static_cast<float>(1.0 - beta2);
+  hipLaunchKernelGGL(lane_scales, dim3((unsigned)sh.g), dim3(kThreads), 0, stream, power,
+                     lane_energy, scale, lanes, len, w_ema);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  DecayArgs d{param, mantissa, gate, lr, wd};
+  const int64_t cpm = (int64_t)sh.m * sh.n / 8;
+  hipLaunchKernelGGL(scale_decay, dim3((unsigned)elementwise_blocks(cpm * sh.g)), dim3(kThreads),
+                     0, stream, u, scale, true, d, sh.m, sh.n, rows, cpm, sh.g);
+  return hipGetLastError();
+}
+
+hipError_t launch_decay(uint16_t* param, uint16_t* mantissa, const uint16_t* u, float wd,
+                        const float* lr, const float* gate, const Shape& sh, hipStream_t stream) {
+  DecayArgs d{param, mantissa, gate, lr, wd};
+  const int64_t cpm = (int64_t)sh.m * sh.n / 8;
+  hipLaunchKernelGGL(scale_decay, dim3((unsigned)elementwise_blocks(cpm * sh.g)), dim3(kThreads),
+                     0, stream, const_cast<uint16_t*>(u), nullptr, false, d, sh.m, sh.n,
+                     sh.m >= sh.n, cpm, sh.g);
+  return hipGetLastError();
+}
+
+}  // namespace anvil

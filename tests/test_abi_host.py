@@ -124,3 +124,54 @@ def test_binding_rejects_cpu_tensors():
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(RuntimeError):
         anvil.load(str(tmp_path / "libanvil.so"))
+
+
+D = 0x50000000
+E = 0x60000000
+F = 0x70000000
+L = 0x80000000
+
+
+def _upd(lib, grad=A, vel=B, out=C, energy=D, param=E, mant=F, lr=L, g=2, m=64, n=32):
+    return lib.anvil_bank_update(grad, vel, 0.95, 0.85, 1.0, out, energy, 0.95, param, mant,
+                                 0.01, lr, g, m, n, None)
+
+
+def test_update_entry_points_reject_before_launching(lib):
+    assert lib.anvil_equalizer_lanes(64, 32) == 64
+    assert lib.anvil_equalizer_lanes(32, 64) == 64
+    assert lib.anvil_equalizer_lanes(48, 48) == 48
+    assert lib.anvil_equalizer_lanes(60, 32) == 0
+    assert lib.anvil_bank_update(None, None, 0.95, 0.85, 1.0, None, None, 0.95, None, None, 0.0,
+                                 None, 0, 64, 32, None) == 0
+    assert lib.anvil_equalize(None, None, 0.95, None, 2, 0, 32, None) == 0
+    assert lib.anvil_decay_update(None, None, None, 0.0, None, None, 0, 8, 8, None) == 0
+    assert _upd(lib, energy=None) == anvil.ANVIL_ERR_INVALID_ARG
+    assert _upd(lib, lr=None) == anvil.ANVIL_ERR_INVALID_ARG
+    assert _upd(lib, g=-2) == anvil.ANVIL_ERR_INVALID_ARG
+    assert _upd(lib, n=36) == anvil.ANVIL_ERR_UNSUPPORTED
+    assert _upd(lib, param=E + 2) == anvil.ANVIL_ERR_MISALIGNED
+    assert _upd(lib, mant=E) == anvil.ANVIL_ERR_ALIAS
+    assert _upd(lib, energy=C + 64) == anvil.ANVIL_ERR_ALIAS
+    assert _upd(lib, lr=F + 16) == anvil.ANVIL_ERR_ALIAS
+    assert _upd(lib, param=B + 4096) == anvil.ANVIL_ERR_ALIAS
+    need = lib.anvil_workspace_bytes(2, 64, 32)
+    args = (A, B, 0.95, 0.85, 1.0, C, D, 0.95, E, F, 0.01, L, 2, 64, 32)
+    assert lib.anvil_bank_update_ws(*args, W, need - 1, None) == anvil.ANVIL_ERR_UNSUPPORTED
+    assert lib.anvil_bank_update_ws(*args, E, need, None) == anvil.ANVIL_ERR_ALIAS
+    assert lib.anvil_bank_update_ws(*args, W + 64, need, None) == anvil.ANVIL_ERR_MISALIGNED
+    assert lib.anvil_equalize(C, D, 0.95, D + 8, 2, 64, 32, None) == anvil.ANVIL_ERR_ALIAS
+    assert lib.anvil_equalize(C + 2, D, 0.95, E, 2, 64, 32, None) == anvil.ANVIL_ERR_MISALIGNED
+    assert lib.anvil_equalize(C, None, 0.95, E, 2, 64, 32, None) == anvil.ANVIL_ERR_INVALID_ARG
+    assert lib.anvil_decay_update(E, F, C, 0.01, L, E, 2, 64, 32, None) == anvil.ANVIL_ERR_ALIAS
+    assert lib.anvil_decay_update(E, F, C, 0.01, L, D + 4, 2, 64, 32, None) == \
+        anvil.ANVIL_ERR_MISALIGNED
+    assert lib.anvil_decay_update(E, F, C, 0.01, None, D, 2, 64, 32, None) == \
+        anvil.ANVIL_ERR_INVALID_ARG
+
+
+def test_workspace_covers_the_equalizer_scratch(lib):
+    for g, m, n in [(24, 2816, 768), (24, 256, 768), (3, 8, 4096)]:
+        lanes = lib.anvil_equalizer_lanes(m, n)
+        base = g * m * n * 2 + 2 * g * min(m, n) ** 2 * 2
+        assert lib.anvil_workspace_bytes(g, m, n) >= base + 2 * g * lanes * 4

@@ -1,0 +1,252 @@
+"""Parity of the rest of the bank update (modded-nanogpt anvil.py, `_rail_equalizer`,
+`_sign_aligned_decay_update`, `anvil_bank_update`) against the oracle, through the C ABI.
+
+Equalizer bar.  The lane powers are fp32 sums of exactly representable squares (bf16 x bf16), so
+any summation order is within (len - 1) * 2^-24 of the exact sum; the oracle rounds an fp64 sum
+once.  Powers, energies and the fp32 scale therefore agree to (len + 2) * 2^-24 relative.  The
+bf16 scales agree except where that tiny difference straddles a bf16 rounding boundary (then they
+are adjacent bf16 values), and given the GPU's own scales the rescaled update is bit-exact.
+
+Decay bar: bit-exact (elementwise fp32 with no contraction on either side)."""
+import numpy as np
+import pytest
+
+from oracle import anvil_oracle as O
+from orthogonalizing_polynomial_cascade_amd import workloads as W
+from tests.helpers import bf16_bits_of, from_gpu, rel_fro, to_gpu_bf16, to_gpu_f32
+
+pytestmark = pytest.mark.gpu
+
+U = 2.0 ** -24
+OUT_TOL = 1e-2
+FLOOR_FACTOR = 1.5
+
+ROW_LANES = [(3, 392, 136), (2, 264, 264), (2, 1096, 136), (1, 8, 8), (2, 72, 8), (1, 1040, 1032),
+             (1, 768, 256)]
+COL_LANES = [(3, 200, 328), (2, 136, 1096), (2, 8, 72), (1, 256, 768), (2, 64, 4104),
+             (1, 1032, 1040)]
+
+
+def _lane_shape(g, m, n):
+    return (g, m, 1) if m >= n else (g, 1, n)
+
+
+def _update_like(rng, g, m, n):
+    """bf16 values with strongly unequal lanes (lognormal row and column scales)."""
+    v = rng.standard_normal((g, m, n)) * np.exp(rng.standard_normal((g, m, 1)))
+    v = v * np.exp(0.5 * rng.standard_normal((g, 1, n)))
+    return O.R((v / np.sqrt(max(m, n))).astype(np.float32))
+
+
+def _gpu_equalize(gpu_lib, u, energy, beta2):
+    import torch
+    g, m, n = u.shape
+    lanes = m if m >= n else n
+    ud = to_gpu_bf16(u)
+    ed = to_gpu_f32(energy.reshape(g, lanes))
+    scratch = torch.empty(2 * g * lanes, dtype=torch.float32, device="cuda")
+    gpu_lib.anvil_equalize(ud, ed, beta2, scratch)
+    s = from_gpu(scratch)
+    shp = _lane_shape(g, m, n)
+    return (from_gpu(ud), from_gpu(ed).reshape(shp), s[:g * lanes].reshape(shp),
+            s[g * lanes:].reshape(shp))
+
+
+def _check_equalizer(u, energy, beta2, out, e_gpu, p_gpu, s_gpu):
+    g, m, n = u.shape
+    length = n if m >= n else m
+    p_or, e_or, s_or = O.equalizer_terms(u, energy, beta2)
+    rtol = (length + 2) * U
+    np.testing.assert_allclose(p_gpu, p_or, rtol=rtol, atol=0)
+    # energy: the power's error enters with weight (1 - beta2) <= the new energy's share of it,
+    # plus a few roundings of the lerp's operands
+    bound = rtol * np.abs(e_or) + 4 * U * (np.abs(energy) + np.abs(p_or)) + 1e-30
+    assert np.all(np.abs(e_gpu - e_or) <= bound), float(np.max(np.abs(e_gpu - e_or) / bound))
+    # scales: equal, or adjacent bf16 values where the fp32 scale sits on a rounding boundary
+    assert np.all(np.abs(s_gpu - s_or) <= 2.0 ** -7 * np.abs(s_or))
+    assert np.mean(s_gpu == s_or) >= 0.97
+    # given the GPU's own bf16 scales the rescale is exact
+    assert np.array_equal(out, O.R(u * s_gpu))
+    want, _ = O.equalizer(u, energy, beta2)
+    assert rel_fro(out, want) <= 2.0 ** -7
+
+
+@pytest.mark.parametrize("g,m,n", ROW_LANES + COL_LANES)
+@pytest.mark.parametrize("beta2", [0.95, 0.0])
+def test_equalize_matches_oracle(gpu_lib, g, m, n, beta2):
+    rng = np.random.default_rng(m * 7 + n * 3 + g + int(beta2 * 100))
+    u = _update_like(rng, g, m, n)
+    power = (u.astype(np.float64) ** 2).mean(axis=-1 if m >= n else -2, keepdims=True)
+    energy = (power * np.exp(rng.standard_normal(power.shape))).astype(np.float32)
+    _check_equalizer(u, energy, beta2, *_gpu_equalize(gpu_lib, u, energy, beta2))
+
+
+def test_equalize_from_zero_energy_and_frozen_ema(gpu_lib):
+    rng = np.random.default_rng(17)
+    g, m, n = 2, 200, 328
+    u = _update_like(rng, g, m, n)
+    zero = np.zeros(_lane_shape(g, m, n), np.float32)
+    _check_equalizer(u, zero, 0.95, *_gpu_equalize(gpu_lib, u, zero, 0.95))
+    # equal energies and beta2 = 1: every lane gets the same gain, the scale is exactly 1
+    flat = np.full(_lane_shape(g, m, n), 0.37, np.float32)
+    out, e, _, s = _gpu_equalize(gpu_lib, u, flat, 1.0)
+    assert np.array_equal(out, u) and np.array_equal(e, flat) and np.all(s == 1.0)
+
+
+def test_equalize_zero_update(gpu_lib):
+    """An all-zero update: every power is 0, the norms clamp at 1e-10 and the update stays 0."""
+    g, m, n = 2, 64, 136
+    u = np.zeros((g, m, n), np.float32)
+    e = np.full(_lane_shape(g, m, n), 0.5, np.float32)
+    out, e_gpu, p, s = _gpu_equalize(gpu_lib, u, e, 0.9)
+    _, e_or, s_or = O.equalizer_terms(u, e, 0.9)
+    assert np.all(out == 0) and np.array_equal(e_gpu, e_or) and np.array_equal(s, s_or)
+
+
+def _decay_inputs(rng, g, m, n):
+    p = O.bf16_bits(rng.standard_normal((g, m, n)).astype(np.float32) * np.float32(0.02))
+    mant = rng.integers(0, 1 << 16, size=(g, m, n), dtype=np.uint32).astype(np.uint16)
+    upd = _update_like(rng, g, m, n)
+    gate = rng.standard_normal((g, m, n)).astype(np.float32)
+    lr = rng.uniform(0.001, 0.05, size=g).astype(np.float32)
+    # edge cases: zero and negative-zero gates and masters, subnormal masters with no update
+    flat_p, flat_m, flat_g, flat_u = (a.reshape(-1) for a in (p, mant, gate, upd))
+    k = flat_p.size
+    idx = rng.choice(k, size=min(k, 64), replace=False)
+    q = len(idx) // 4
+    flat_g[idx[:q]] = 0.0
+    flat_g[idx[q:2 * q]] = -0.0
+    flat_p[idx[2 * q:3 * q]] = np.array([0x0000, 0x8000], np.uint16)[np.arange(3 * q - 2 * q) % 2]
+    flat_m[idx[2 * q:3 * q:2]] = 0
+    flat_u[idx[2 * q:]] = 0.0
+    return p, mant, upd, gate, lr
+
+
+@pytest.mark.parametrize("g,m,n", [(3, 200, 328), (2, 392, 136), (1, 8, 8), (2, 1096, 136)])
+def test_decay_bit_exact(gpu_lib, g, m, n):
+    import torch
+    rng = np.random.default_rng(g + m + n)
+    p, mant, upd, gate, lr = _decay_inputs(rng, g, m, n)
+    wd = 0.0125
+    pd = torch.from_numpy(p.view(np.int16)).cuda().view(torch.bfloat16)
+    md = torch.from_numpy(mant.view(np.int16)).cuda()
+    gpu_lib.anvil_decay_update(pd, md, to_gpu_bf16(upd), wd, to_gpu_f32(lr), to_gpu_f32(gate))
+    p_want, m_want = O.decay_update(p, mant, upd, wd, lr, gate)
+    assert np.array_equal(bf16_bits_of(pd), p_want)
+    assert np.array_equal(md.cpu().numpy().view(np.uint16), m_want)
+
+
+def _state(rng, g, m, n):
+    p = O.bf16_bits(rng.standard_normal((g, m, n)).astype(np.float32) * np.float32(0.02))
+    mant = rng.integers(0, 1 << 16, size=(g, m, n), dtype=np.uint32).astype(np.uint16)
+    lr = rng.uniform(0.01, 0.05, size=g).astype(np.float32)
+    return p, mant, lr
+
+
+def _gpu_tensors(p, mant, energy, lr):
+    import torch
+    return (torch.from_numpy(p.view(np.int16).copy()).cuda().view(torch.bfloat16),
+            torch.from_numpy(mant.view(np.int16).copy()).cuda(),
+            to_gpu_f32(energy.reshape(energy.shape[0], -1)), to_gpu_f32(lr))
+
+
+@pytest.mark.parametrize("g,m,n", [(3, 200, 328), (3, 392, 136), (2, 264, 264), (2, 1096, 136)])
+def test_bank_update_composes_the_stages(gpu_lib, g, m, n):
+    """The fused update equals the step, then the oracle's equalizer on the step's output, then the
+    oracle's decay gated on the slow rail the step wrote (the GPU's own cascade output as input, so
+    the comparison is at stage precision)."""
+    import torch
+    rng = np.random.default_rng(5 * m + n)
+    w = W.gaussian(g, m, n, seed=3, steps=range(2))
+    p, mant, lr = _state(rng, g, m, n)
+    energy = np.zeros(_lane_shape(g, m, n), np.float32)
+    vel = torch.zeros((2, g, m, n), dtype=torch.float32, device="cuda")
+    vel_ref = vel.clone()
+    pd, md, ed, lrd = _gpu_tensors(p, mant, energy, lr)
+    wd = 0.0125
+    for t in range(2):
+        G = to_gpu_f32(w.grad(t))
+        step_out = from_gpu(gpu_lib.anvil_bank_step(G, vel_ref, 0.95, 0.85, 1.0))
+        upd = gpu_lib.anvil_bank_update(G, vel, 0.95, 0.85, 1.0, ed, 0.95, pd, md, wd, lrd)
+        torch.cuda.synchronize()
+        assert torch.equal(vel, vel_ref)
+        e_prev = energy
+        out_gpu = from_gpu(upd)
+        e_gpu = from_gpu(ed).reshape(energy.shape)
+        # the equalizer's outputs, checked as in the stage test (scales recovered from the output
+        # are not available here, so compare with the oracle's scales at one bf16 ulp)
+        want, e_or = O.equalizer(step_out, e_prev, 0.95)
+        assert rel_fro(out_gpu, want) <= 2.0 ** -7
+        length = n if m >= n else m
+        np.testing.assert_allclose(e_gpu, e_or, rtol=(length + 8) * U, atol=1e-30)
+        p_want, m_want = O.decay_update(p, mant, out_gpu, wd, lr, from_gpu(vel)[1])
+        p, mant = bf16_bits_of(pd), md.cpu().numpy().view(np.uint16)
+        assert np.array_equal(p, p_want) and np.array_equal(mant, m_want)
+        energy = e_gpu
+
+
+@pytest.mark.parametrize("g,m,n", [(2, 200, 328), (2, 392, 136), (2, 264, 264), (1, 1096, 136)])
+def test_bank_update_end_to_end(gpu_lib, g, m, n):
+    """Two whole updates on the GPU against the oracle's `bank_update`, each side carrying its own
+    state.  Bars: the update as in the bank-step tests (1e-2 relative Frobenius, or 1.5x the
+    oracle's own fp64/fp32 drift); the rails within 1e-6; the per-lane energies and the change
+    of the fp32 master within twice the update bar (they are quadratic and linear in it)."""
+    import torch
+    rng = np.random.default_rng(9 * m + n)
+    w = W.gaussian(g, m, n, seed=11, steps=range(2))
+    p, mant, lr = _state(rng, g, m, n)
+    energy = np.zeros(_lane_shape(g, m, n), np.float32)
+    vel = torch.zeros((2, g, m, n), dtype=torch.float32, device="cuda")
+    pd, md, ed, lrd = _gpu_tensors(p, mant, energy, lr)
+    v_or = np.zeros((2, g, m, n), np.float32)
+    p_or, m_or, e_or = p, mant, energy
+    wd = 0.0125
+    for t in range(2):
+        Gn = w.grad(t)
+        v_prev = v_or
+        master_old = ((p_or.astype(np.uint32) << 16) | m_or).view(np.float32)
+        upd = from_gpu(gpu_lib.anvil_bank_update(to_gpu_f32(Gn), vel, 0.95, 0.85, 1.0, ed, 0.95,
+                                                 pd, md, wd, lrd))
+        u_or, v_or, e_or, p_or, m_or = O.bank_update(Gn, v_or, 0.95, 0.85, 1.0, e_or, 0.95, p_or,
+                                                     m_or, wd, lr)
+        u_or = O.bf16_to_f32(u_or)
+        v_gpu = from_gpu(vel)
+        assert np.max(np.abs(v_gpu - v_or) / np.maximum(np.abs(v_or), 1e-30)) <= 1e-6
+        tol = OUT_TOL
+        for i in range(g):
+            r = rel_fro(upd[i], u_or[i])
+            if r > OUT_TOL:
+                X = O.R(O.momentum_step(Gn[i:i + 1], v_prev[:, i:i + 1], 0.95, 0.85, 1.0)[1])
+                floor = rel_fro(O.cascade(X, acc="fp32")[0], O.cascade(X)[0])
+                tol = max(tol, FLOOR_FACTOR * floor)
+            assert r <= max(OUT_TOL, tol), f"step {t} matrix {i}: update {r:.3e}"
+        e_gpu = from_gpu(ed).reshape(e_or.shape)
+        assert rel_fro(e_gpu, e_or) <= 2 * tol
+        master_gpu = ((bf16_bits_of(pd).astype(np.uint32) << 16) |
+                      md.cpu().numpy().view(np.uint16)).view(np.float32)
+        master_or = ((p_or.astype(np.uint32) << 16) | m_or).view(np.float32)
+        d_gpu = master_gpu.astype(np.float64) - master_old
+        d_or = master_or.astype(np.float64) - master_old
+        assert rel_fro(d_gpu, d_or) <= 2 * tol
+
+
+def test_bank_update_workspace_variant_is_identical(gpu_lib):
+    import torch
+    g, m, n = 2, 200, 328
+    rng = np.random.default_rng(23)
+    G = to_gpu_f32(rng.standard_normal((g, m, n)).astype(np.float32))
+    p, mant, lr = _state(rng, g, m, n)
+    e = np.abs(rng.standard_normal(_lane_shape(g, m, n))).astype(np.float32)
+    runs = []
+    for use_ws in (False, True):
+        vel = torch.zeros((2, g, m, n), dtype=torch.float32, device="cuda")
+        pd, md, ed, lrd = _gpu_tensors(p, mant, e, lr)
+        ws = None
+        if use_ws:
+            ws = torch.empty(gpu_lib.workspace_bytes(g, m, n), dtype=torch.uint8, device="cuda")
+        u = gpu_lib.anvil_bank_update(G, vel, 0.95, 0.85, 0.4385, ed, 0.95, pd, md, 0.01, lrd,
+                                      workspace=ws)
+        runs.append([bf16_bits_of(u), bf16_bits_of(pd), md.cpu().numpy(), from_gpu(ed),
+                     from_gpu(vel)])
+    for a, b in zip(*runs):
+        assert np.array_equal(a, b)
