@@ -97,6 +97,64 @@ def time_bank_step(anvil, w, steps, warmup):
     return ms, wall, (G, vel, out)
 
 
+def update_tensors(anvil, w):
+    import torch
+    from orthogonalizing_polynomial_cascade_amd import workloads
+    st = workloads.update_state(w)
+    dev = torch.device("cuda:0")
+    pb = torch.from_numpy(st.param_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    mt = torch.from_numpy(st.mantissa.view(np.int16)).to(dev)
+    en = torch.from_numpy(st.lane_energy).to(dev)
+    lr = torch.from_numpy(st.eff_lr).to(dev)
+    return st, pb, mt, en, lr
+
+
+def time_bank_update(anvil, w, steps, warmup):
+    """The whole bank update (step, equalizer, decay) and its tail kernels alone."""
+    import torch
+    g, m, n = w.g, w.m, w.n
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    G = torch.from_numpy(w.grad(w.measured[0])).to(dev)
+    vel = torch.zeros((2, g, m, n), dtype=torch.float32, device=dev)
+    out = torch.empty((g, m, n), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(anvil.workspace_bytes(g, m, n), dtype=torch.uint8, device=dev)
+    st, pb, mt, en, lr = update_tensors(anvil, w)
+    mu, fb, fw = anvil.rail_scalars(w.step_ids[w.measured[0]])
+
+    def upd():
+        anvil.anvil_bank_update(G, vel, mu, fb, fw, en, st.beta2, pb, mt, st.eff_wd, lr,
+                                update=out, workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        upd()
+    torch.cuda.synchronize()
+    e0, e1 = _events()
+    e0.record(stream)
+    for _ in range(steps):
+        upd()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    res = {"ms_per_update": e0.elapsed_time(e1) / steps}
+    lanes = anvil.equalizer_lanes(m, n)
+    scratch = torch.empty(2 * g * lanes, dtype=torch.float32, device=dev)
+    gate = vel[1]
+    reps = 20
+    for name, fn in (("equalize", lambda: anvil.anvil_equalize(out, en, 1.0, scratch, stream=stream)),
+                     ("decay", lambda: anvil.anvil_decay_update(pb, mt, out, st.eff_wd, lr, gate,
+                                                                stream=stream))):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = _events()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[f"{name}_us"] = e0.elapsed_time(e1) / reps * 1e3
+    return res
+
+
 def time_stages(anvil, w, reps=20):
     """Average duration of each stage kernel (HIP events around `reps` launches on one stream)."""
     import torch
@@ -246,6 +304,20 @@ def main():
                      "traffic_unit": "bytes per launch",
                      "algorithmic_bytes": 2 * w.g * (2 * w.m * w.n + min(w.m, w.n) ** 2),
                      "flops_per_launch": apply_flops},
+    }
+    # the rest of the bank update (equalizer and decay) on the same workload, timed after the
+    # headline step; its tail is HBM-bound at 18 bytes per element (lane powers read the update,
+    # the fused rescale-and-decay pass moves 16)
+    u = time_bank_update(anvil, w, max(10, args.steps // 2), args.warmup)
+    count = w.g * w.m * w.n
+    tail_ms = u["ms_per_update"] - rec["ms_per_step"]
+    line["bank_update"] = {
+        "ms_per_update": u["ms_per_update"],
+        "matrices_per_s": w.g / (u["ms_per_update"] * 1e-3),
+        "tail_us": tail_ms * 1e3,
+        "tail_gbs": 18 * count / (tail_ms * 1e-3) / 1e9 if tail_ms > 0 else None,
+        "equalize_us": u["equalize_us"], "equalize_gbs": 6 * count / (u["equalize_us"] * 1e-6) / 1e9,
+        "decay_us": u["decay_us"], "decay_gbs": 14 * count / (u["decay_us"] * 1e-6) / 1e9,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)

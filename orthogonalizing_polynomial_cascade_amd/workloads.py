@@ -177,6 +177,31 @@ def scaled(w: Workload, g: int | None = None, m: int | None = None, n: int | Non
     return Workload(w.name, g or w.g, m or w.m, n or w.n, list(w.step_ids), list(w.measured))
 
 
+@dataclass
+class UpdateState:
+    """Parameter-side inputs of a whole bank update for a [g, m, n] bank (synthetic values: the
+    page names the fields but not their magnitudes)."""
+    param_bits: np.ndarray    # uint16 [g, m, n]: high halves of N(0, 0.02^2) fp32 masters
+    mantissa: np.ndarray      # uint16 [g, m, n]: their low halves
+    lane_energy: np.ndarray   # fp32 [g, lanes]: zeros (a fresh optimizer)
+    eff_lr: np.ndarray        # fp32 [g]: 0.02, doubled on odd matrices of the mlp bank
+    eff_wd: float             # 0.02 * 0.025: an lr times a weight decay
+    beta2: float              # 0.95
+
+
+def update_state(w: Workload, g: int | None = None, seed: int = 7) -> UpdateState:
+    """fp32 master weights N(0, 0.02^2) stored the page's way: the high 16 bits as the bf16
+    parameter, the low 16 bits as the mantissa."""
+    g = w.g if g is None else g
+    r = _rng(seed + 31 * w.m + w.n)
+    master = (r.standard_normal((g, w.m, w.n)) * 0.02).astype(F32).view(np.uint32)
+    lanes = w.m if w.m >= w.n else w.n
+    mult = [2.0 if (w.name == "mlp" and i % 2 == 1) else 1.0 for i in range(g)]
+    eff_lr = np.array([0.02 * k for k in mult], dtype=F32)
+    return UpdateState((master >> np.uint32(16)).astype(np.uint16),
+                       (master & np.uint32(0xFFFF)).astype(np.uint16),
+                       np.zeros((g, lanes), F32), eff_lr, 0.02 * 0.025, 0.95)
+
 ALL = {
     "single_wide": single_wide,
     "qk": qk_bank,
