@@ -90,6 +90,18 @@ int anvil_bank_step_ws(const float* grad, float* velocity, float momentum, float
                        float fast_weight, uint16_t* out, int64_t g, int64_t m, int64_t n,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* The bank step with a caller-chosen table of quintic maps (the page's cascade loop with another
+ * coefficient list and step count, e.g. a plain quintic Newton-Schulz iteration).
+ *   maps        HOST array of `steps` triples (a, b, c), fp32, applied in order exactly as the
+ *               six ANVIL maps are: B = b A + c A A, then X <- a X + X B (tall) or a X + B X.
+ *   steps       1 .. 16 (else ANVIL_ERR_INVALID_ARG).
+ *   workspace   a caller workspace as for anvil_bank_step_ws, or NULL for the cached one.
+ * With the ANVIL table and steps = 6 the result is identical to anvil_bank_step. */
+int anvil_bank_step_maps(const float* grad, float* velocity, float momentum, float fast_beta,
+                         float fast_weight, const float* maps, int steps, uint16_t* out,
+                         int64_t g, int64_t m, int64_t n, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
 /* Workspace bytes for a [g, m, n] bank step or bank update (0 for an empty stack, or for
  * unsupported sizes). */
 size_t anvil_workspace_bytes(int64_t g, int64_t m, int64_t n);

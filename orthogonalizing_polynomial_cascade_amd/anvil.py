@@ -43,6 +43,8 @@ SIGNATURES = {
     "anvil_bank_update_ws": (_i, [_vp, _vp, _f, _f, _f, _vp, _vp, _d, _vp, _vp, _f, _vp,
                                   _i64, _i64, _i64, _vp, _sz, _vp]),
     "anvil_equalizer_lanes": (_i64, [_i64, _i64]),
+    "anvil_bank_step_maps": (_i, [_vp, _vp, _f, _f, _f, _vp, _i, _vp, _i64, _i64, _i64, _vp, _sz,
+                                  _vp]),
     "anvil_equalize": (_i, [_vp, _vp, _d, _vp, _i64, _i64, _i64, _vp]),
     "anvil_decay_update": (_i, [_vp, _vp, _vp, _f, _vp, _vp, _i64, _i64, _i64, _vp]),
 }
@@ -151,6 +153,32 @@ def anvil_bank_step(grad, velocity, momentum, fast_beta, fast_weight, out=None, 
                                     _ptr(out), g, m, n, _ptr(workspace), workspace.numel(),
                                     _stream(stream))
         _check("anvil_bank_step_ws", st)
+    return out
+
+
+def anvil_bank_step_maps(grad, velocity, momentum, fast_beta, fast_weight, maps, out=None,
+                         workspace=None, stream=None):
+    """The bank step with a caller-chosen list of (a, b, c) quintic maps (1 to 16 of them)."""
+    import torch
+    lib = load()
+    _need(grad, "grad", torch.float32)
+    g, m, n = _gmn(grad)
+    _need(velocity, "velocity", torch.float32, (2, g, m, n))
+    table = [float(v) for abc in maps for v in abc]
+    if len(table) != 3 * len(maps):
+        raise ValueError("maps must be (a, b, c) triples")
+    host = (ctypes.c_float * max(1, len(table)))(*table)
+    if out is None:
+        out = torch.empty((g, m, n), dtype=torch.bfloat16, device=grad.device)
+    _need(out, "out", torch.bfloat16, (g, m, n))
+    ws, wsb = None, 0
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8)
+        ws, wsb = _ptr(workspace), workspace.numel()
+    _check("anvil_bank_step_maps", lib.anvil_bank_step_maps(
+        _ptr(grad), _ptr(velocity), momentum, fast_beta, fast_weight,
+        ctypes.cast(host, ctypes.c_void_p), len(maps), _ptr(out), g, m, n, ws, wsb,
+        _stream(stream)))
     return out
 
 

@@ -13,8 +13,8 @@ namespace {
 
 using anvil::Shape;
 
-// The six quintic maps (a, b, c) in application order (anvil.py, the table of maps), taken as
-// fp32 kernel arguments.
+// The six quintic maps (a, b, c) in application order (anvil.py, the table of maps); the kernels
+// take them as fp32 values of these doubles.
 const double kMaps[6][3] = {
     {3.923798038567, -6.095026865488, 3.905234618423},
     {3.278126713798, -3.328923386476, 0.989127286973},
@@ -23,6 +23,15 @@ const double kMaps[6][3] = {
     {2.245503932403, -2.443826979899, 0.963091710461},
     {2.256537145403, -2.166840097229, 0.929501253245},
 };
+struct MapTable {
+  float v[6][3];
+  MapTable() {
+    for (int k = 0; k < 6; ++k)
+      for (int j = 0; j < 3; ++j) v[k][j] = static_cast<float>(kMaps[k][j]);
+  }
+};
+const MapTable kAnvilMaps;
+constexpr int kMaxMaps = 16;
 
 // Banks with more rows than this use the split (two-rounding) apply (anvil.py).
 constexpr int64_t kSplitMinRows = 1024;
@@ -97,11 +106,12 @@ int check_step_args(const float* grad, float* velocity, uint16_t* out, const Sha
   return ANVIL_OK;
 }
 
-// The launch sequence: momentum, Gram 0 with trace, normalise, then six (Gram, poly, apply).
-// X starts in `out`; the apply ping-pongs between `out` and the workspace copy, and after the
-// sixth (an even number of) swaps the result is back in `out`.
+// The launch sequence: momentum, Gram 0 with trace, normalise, then per map (Gram, poly, apply).
+// The apply ping-pongs between `out` and the workspace copy; X starts in `out` for an even number
+// of maps and in the workspace copy for an odd number, so that the last apply writes `out`.
 int run_step(const float* grad, float* velocity, float momentum, float fast_beta,
-             float fast_weight, uint16_t* out, const Shape& sh, char* ws, hipStream_t stream) {
+             float fast_weight, uint16_t* out, const Shape& sh, char* ws, hipStream_t stream,
+             const float (*maps)[3] = kAnvilMaps.v, int steps = 6) {
   const Layout l = layout_for(sh);
   uint16_t* ping = reinterpret_cast<uint16_t*>(ws + l.ping);
   uint16_t* A = reinterpret_cast<uint16_t*>(ws + l.a);
@@ -111,24 +121,23 @@ int run_step(const float* grad, float* velocity, float momentum, float fast_beta
   const int64_t count = sh.g * sh.m * sh.n;
   const bool split = sh.m > kSplitMinRows;
 
-  hipError_t e = anvil::launch_momentum(grad, velocity, velocity + count, out, count, momentum,
+  uint16_t* X = (steps % 2 == 0) ? out : ping;
+  uint16_t* Y = (steps % 2 == 0) ? ping : out;
+  hipError_t e = anvil::launch_momentum(grad, velocity, velocity + count, X, count, momentum,
                                         fast_beta, fast_weight, stream);
   if (e != hipSuccess) return hip_status(e);
-  uint16_t* X = out;
-  uint16_t* Y = ping;
   e = anvil::launch_gram(X, A, partials, sh, stream);
   if (e != hipSuccess) return hip_status(e);
   e = anvil::launch_normalize(X, A, partials, d, sh, stream);
   if (e != hipSuccess) return hip_status(e);
-  for (int k = 0; k < 6; ++k) {
+  for (int k = 0; k < steps; ++k) {
     if (k > 0) {
       e = anvil::launch_gram(X, A, nullptr, sh, stream);
       if (e != hipSuccess) return hip_status(e);
     }
-    e = anvil::launch_poly(A, B, static_cast<float>(kMaps[k][1]), static_cast<float>(kMaps[k][2]),
-                           sh.g, sh.s(), stream);
+    e = anvil::launch_poly(A, B, maps[k][1], maps[k][2], sh.g, sh.s(), stream);
     if (e != hipSuccess) return hip_status(e);
-    e = anvil::launch_apply(X, B, Y, static_cast<float>(kMaps[k][0]), split, sh, stream);
+    e = anvil::launch_apply(X, B, Y, maps[k][0], split, sh, stream);
     if (e != hipSuccess) return hip_status(e);
     std::swap(X, Y);
   }
@@ -273,6 +282,34 @@ int anvil_bank_step(const float* grad, float* velocity, float momentum, float fa
   st = cached_workspace(layout_for(sh).total, hs, &ws);
   if (st != ANVIL_OK) return st;
   return run_step(grad, velocity, momentum, fast_beta, fast_weight, out, sh, ws, hs);
+}
+
+int anvil_bank_step_maps(const float* grad, float* velocity, float momentum, float fast_beta,
+                         float fast_weight, const float* maps, int steps, uint16_t* out,
+                         int64_t g, int64_t m, int64_t n, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (steps < 1 || steps > kMaxMaps) return ANVIL_ERR_INVALID_ARG;
+  Shape sh;
+  bool empty = false;
+  int st = check_shape(g, m, n, &sh, &empty);
+  if (st != ANVIL_OK || empty) return st;
+  if (!maps) return ANVIL_ERR_INVALID_ARG;
+  st = check_step_args(grad, velocity, out, sh);
+  if (st != ANVIL_OK) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  char* ws = nullptr;
+  if (workspace) {
+    st = check_workspace(workspace, workspace_bytes, grad, velocity, out, sh);
+    if (st != ANVIL_OK) return st;
+    ws = static_cast<char*>(workspace);
+  } else {
+    st = cached_workspace(layout_for(sh).total, hs, &ws);
+    if (st != ANVIL_OK) return st;
+  }
+  float table[kMaxMaps][3];
+  for (int k = 0; k < steps; ++k)
+    for (int j = 0; j < 3; ++j) table[k][j] = maps[3 * k + j];
+  return run_step(grad, velocity, momentum, fast_beta, fast_weight, out, sh, ws, hs, table, steps);
 }
 
 int anvil_bank_update(const float* grad, float* velocity, float momentum, float fast_beta,

@@ -175,3 +175,23 @@ def test_workspace_covers_the_equalizer_scratch(lib):
         lanes = lib.anvil_equalizer_lanes(m, n)
         base = g * m * n * 2 + 2 * g * min(m, n) ** 2 * 2
         assert lib.anvil_workspace_bytes(g, m, n) >= base + 2 * g * lanes * 4
+
+
+def test_map_table_entry_point_checks(lib):
+    table = (ctypes.c_float * 6)(3.0, -4.0, 2.0, 3.0, -4.0, 2.0)
+    tp = ctypes.cast(table, ctypes.c_void_p)
+    args = (A, B, 0.95, 0.85, 1.0)
+    assert lib.anvil_bank_step_maps(*args, tp, 0, C, 2, 64, 32, None, 0, None) == \
+        anvil.ANVIL_ERR_INVALID_ARG
+    assert lib.anvil_bank_step_maps(*args, tp, 17, C, 2, 64, 32, None, 0, None) == \
+        anvil.ANVIL_ERR_INVALID_ARG
+    assert lib.anvil_bank_step_maps(*args, None, 2, C, 2, 64, 32, None, 0, None) == \
+        anvil.ANVIL_ERR_INVALID_ARG
+    assert lib.anvil_bank_step_maps(*args, tp, 2, C, 0, 64, 32, None, 0, None) == 0
+    assert lib.anvil_bank_step_maps(*args, tp, 2, A, 2, 64, 32, None, 0, None) == \
+        anvil.ANVIL_ERR_ALIAS
+    need = lib.anvil_workspace_bytes(2, 64, 32)
+    assert lib.anvil_bank_step_maps(*args, tp, 2, C, 2, 64, 32, W, need - 1, None) == \
+        anvil.ANVIL_ERR_UNSUPPORTED
+    assert lib.anvil_bank_step_maps(*args, tp, 2, C, 2, 64, 32, W + 32, need, None) == \
+        anvil.ANVIL_ERR_MISALIGNED

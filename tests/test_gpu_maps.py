@@ -1,0 +1,76 @@
+"""The bank step with a caller-chosen map table (anvil_bank_step_maps) against the oracle's
+cascade with the same table: the page's cascade loop with another coefficient list and step count.
+
+Bars as for the bank step: relative Frobenius <= 1e-2 per matrix on the update (or 1.5x the
+oracle's own fp64/fp32-accumulation drift on inputs outside the maps' window), rails bit-exact."""
+import numpy as np
+import pytest
+
+from oracle import anvil_oracle as O
+from orthogonalizing_polynomial_cascade_amd import workloads as W
+from tests.helpers import bf16_bits_of, from_gpu, rel_fro, to_gpu_f32
+
+pytestmark = pytest.mark.gpu
+
+NS5 = [(3.4445, -4.7750, 2.0315)] * 5
+TABLES = {"ns5": NS5, "anvil3": list(O.ANVIL_MAPS[:3]), "anvil1": list(O.ANVIL_MAPS[:1]),
+          "anvil_x2": list(O.ANVIL_MAPS) + list(O.ANVIL_MAPS)}
+SHAPES = [(3, 200, 328), (3, 392, 136), (2, 264, 264), (2, 1096, 136), (1, 8, 16)]
+
+
+def _check(got, want_fn, X, g):
+    for i in range(g):
+        r = rel_fro(got[i], want_fn(X[i:i + 1])[0])
+        if r > 1e-2:
+            floor = rel_fro(want_fn(X[i:i + 1], acc="fp32")[0], want_fn(X[i:i + 1])[0])
+            assert r <= 1.5 * floor, f"matrix {i}: {r:.3e} (floor {floor:.3e})"
+
+
+@pytest.mark.parametrize("name", list(TABLES))
+@pytest.mark.parametrize("g,m,n", SHAPES)
+def test_map_table_matches_oracle(gpu_lib, name, g, m, n):
+    import torch
+    maps = TABLES[name]
+    G = W.gaussian(g, m, n, seed=5).grad(0)
+    vel = torch.zeros((2, g, m, n), dtype=torch.float32, device="cuda")
+    out = from_gpu(gpu_lib.anvil_bank_step_maps(to_gpu_f32(G), vel, 0.95, 0.85, 1.0, maps))
+    v_want, y = O.momentum_step(G, np.zeros((2, g, m, n), np.float32), 0.95, 0.85, 1.0)
+    assert np.array_equal(from_gpu(vel).view(np.uint32), v_want.view(np.uint32))
+    X = O.R(y)
+    _check(out, lambda x, acc="fp64": O.cascade(x, maps=maps, acc=acc), X, g)
+    if name == "ns5":
+        # the quintic Newton-Schulz band, on inputs whose normalised spectrum starts inside the
+        # window [0.01, 1] that five steps lift into it (square Gaussians start far below)
+        for i in range(g):
+            x = X[i].astype(np.float64)
+            s_in = np.linalg.svd(x, compute_uv=False) / (np.sqrt(np.sum(x * x)) * 1.05)
+            if s_in.min() < 0.01:
+                continue
+            s = np.linalg.svd(out[i].astype(np.float64), compute_uv=False)
+            assert s.min() > 0.55 and s.max() < 1.3, (s.min(), s.max())
+
+
+def test_anvil_table_equals_bank_step(gpu_lib):
+    import torch
+    g, m, n = 3, 392, 136
+    G = to_gpu_f32(W.gaussian(g, m, n, seed=8).grad(0))
+    v1 = torch.zeros((2, g, m, n), dtype=torch.float32, device="cuda")
+    v2 = v1.clone()
+    a = gpu_lib.anvil_bank_step(G, v1, 0.95, 0.85, 0.4385)
+    ws = torch.empty(gpu_lib.workspace_bytes(g, m, n), dtype=torch.uint8, device="cuda")
+    b = gpu_lib.anvil_bank_step_maps(G, v2, 0.95, 0.85, 0.4385, list(O.ANVIL_MAPS), workspace=ws)
+    assert np.array_equal(bf16_bits_of(a), bf16_bits_of(b))
+    assert torch.equal(v1, v2)
+
+
+def test_table_length_limits(gpu_lib):
+    import torch
+    g, m, n = 1, 64, 32
+    G = to_gpu_f32(np.ones((g, m, n), np.float32))
+    vel = torch.zeros((2, g, m, n), dtype=torch.float32, device="cuda")
+    with pytest.raises(gpu_lib.AnvilError):
+        gpu_lib.anvil_bank_step_maps(G, vel, 0.95, 0.85, 1.0, [])
+    with pytest.raises(gpu_lib.AnvilError):
+        gpu_lib.anvil_bank_step_maps(G, vel, 0.95, 0.85, 1.0, NS5 * 4)
+    out = gpu_lib.anvil_bank_step_maps(G, vel, 0.95, 0.85, 1.0, (NS5 * 4)[:16])
+    assert torch.isfinite(out.float()).all()

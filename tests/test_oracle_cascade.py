@@ -181,3 +181,36 @@ def test_noise_floor_of_warmed_mlp_input():
     warmed = floor(X)
     assert fresh < 6e-3
     assert warmed > 1.5 * fresh
+
+
+# A plain 5-step quintic Newton-Schulz table (the same iteration with one repeated map), and an
+# odd-length prefix of the ANVIL table: the closed form holds for any list of maps.
+NS5 = [(3.4445, -4.7750, 2.0315)] * 5
+ANVIL3 = list(O.ANVIL_MAPS[:3])
+
+
+def _F_of(maps, s):
+    s = np.asarray(s, dtype=np.float64)
+    for a, b, c in maps:
+        s = a * s + b * s ** 3 + c * s ** 5
+    return s
+
+
+@pytest.mark.parametrize("maps", [NS5, ANVIL3], ids=["ns5", "anvil3"])
+@pytest.mark.parametrize("shape", [(8, 24), (24, 8), (16, 16), (48, 32)])
+def test_exact_mode_with_other_map_tables(maps, shape):
+    rng = np.random.default_rng(3 * sum(shape))
+    X = rng.standard_normal(shape)
+    got = O.cascade(X[None], exact=True, maps=maps)[0]
+    U, S, Vt = np.linalg.svd(X, full_matrices=False)
+    d = np.sqrt(np.sum(X ** 2)) * 1.05 + 1e-6
+    want = (U * _F_of(maps, S / d)[None, :]) @ Vt
+    np.testing.assert_allclose(got, want, rtol=1e-9, atol=1e-12)
+
+
+def test_ns5_table_lands_in_its_band():
+    """The quintic Newton-Schulz map's known behaviour: it does not converge to exactly 1 but sends
+    [0.01, 1] into roughly [0.68, 1.2] after five steps (its fixed-point oscillation band)."""
+    s = np.linspace(0.01, 1.0, 5001)
+    f = _F_of(NS5, s)
+    assert np.all((f > 0.6) & (f < 1.25))
