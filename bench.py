@@ -155,6 +155,49 @@ def time_bank_update(anvil, w, steps, warmup):
     return res
 
 
+def time_contract(anvil, w, steps, warmup):
+    """The whole update in the page's bank contract: bf16 gradient, device scalars, fixed buffers,
+    captured once into a HIP graph and replayed; against the same call made eagerly."""
+    import torch
+    g, m, n = w.g, w.m, w.n
+    dev = torch.device("cuda:0")
+    G = torch.from_numpy(w.grad(w.measured[0])).to(dev).to(torch.bfloat16)
+    vel = torch.zeros((2, g, m, n), dtype=torch.float32, device=dev)
+    out = torch.empty((g, m, n), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(anvil.workspace_bytes(g, m, n), dtype=torch.uint8, device=dev)
+    st, pb, mt, en, lr = update_tensors(anvil, w)
+    mu, fb, fw = anvil.rail_scalars(w.step_ids[w.measured[0]])
+    scal = torch.tensor([mu, fb, fw, st.eff_wd], dtype=torch.float32, device=dev)
+
+    def call():
+        anvil.anvil_bank_update_dev(G, vel, scal, out, en, st.beta2, pb, mt, lr, ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(max(1, warmup)):
+            call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    res = {}
+    for name, fn in (("eager", call), ("graph", graph.replay)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = _events()
+        stream = torch.cuda.current_stream()
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[f"{name}_ms_per_update"] = e0.elapsed_time(e1) / steps
+    return res
+
+
 def time_stages(anvil, w, reps=20):
     """Average duration of each stage kernel (HIP events around `reps` launches on one stream)."""
     import torch
@@ -319,6 +362,9 @@ def main():
         "equalize_us": u["equalize_us"], "equalize_gbs": 6 * count / (u["equalize_us"] * 1e-6) / 1e9,
         "decay_us": u["decay_us"], "decay_gbs": 14 * count / (u["decay_us"] * 1e-6) / 1e9,
     }
+    # the page's bank contract: bf16 gradient, device scalars, one graph replay per update
+    c = time_contract(anvil, w, max(10, args.steps // 2), args.warmup)
+    line["bank_update"]["bf16_grad_device_scalars"] = c
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)

@@ -54,6 +54,12 @@ enum anvil_status {
   ANVIL_ERR_HIP = 6          /* a HIP API or launch error; see anvil_last_hip_error() */
 };
 
+/* Gradient element types of the device-scalar entry points. */
+enum anvil_grad_dtype {
+  ANVIL_GRAD_F32 = 0,  /* fp32 [g, m, n] */
+  ANVIL_GRAD_BF16 = 1  /* bf16 bits [g, m, n]; widened to fp32 exactly before the rail lerps */
+};
+
 /* Static, NUL-terminated description of a status code. */
 const char* anvil_status_string(int status);
 
@@ -201,6 +207,30 @@ int anvil_equalize(uint16_t* update, float* lane_energy, double beta2, float* la
 int anvil_decay_update(uint16_t* param, uint16_t* mantissa, const uint16_t* update, float eff_wd,
                        const float* eff_lr, const float* gate, int64_t g, int64_t m, int64_t n,
                        void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * The page's bank contract (anvil.py, `AnvilBank` and `anvil_bank_update`): a bf16 (or fp32)
+ * gradient, the per-step scalars as device values read when the kernels run, fixed caller
+ * buffers and a caller workspace.  These calls allocate nothing, never synchronise and read no
+ * device value on the host, so a sequence of them can be captured into a HIP graph and replayed
+ * with new gradients and scalars written into the same buffers between replays.  The first call
+ * for a given shape must run outside capture (it sets kernel attributes once).
+ *
+ *   grad        fp32 or bf16 [g, m, n] per grad_dtype (enum anvil_grad_dtype), read only.
+ *   scalars     DEVICE fp32 array: [0] momentum, [1] fast_beta, [2] fast_weight, and for the
+ *               update [3] eff_wd; the caller refreshes it (one host-to-device copy per step).
+ *   workspace   required (anvil_workspace_bytes(g, m, n) bytes, 256-byte aligned).
+ * Everything else as in anvil_bank_step / anvil_bank_update.
+ * ------------------------------------------------------------------------------------------ */
+int anvil_bank_step_dev(const void* grad, int grad_dtype, float* velocity, const float* scalars,
+                        uint16_t* out, int64_t g, int64_t m, int64_t n, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+int anvil_bank_update_dev(const void* grad, int grad_dtype, float* velocity,
+                          const float* scalars, uint16_t* update, float* lane_energy,
+                          double beta2, uint16_t* param, uint16_t* mantissa,
+                          const float* eff_lr, int64_t g, int64_t m, int64_t n, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

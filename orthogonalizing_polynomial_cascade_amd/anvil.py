@@ -21,6 +21,9 @@ ANVIL_ERR_ALIAS = 4
 ANVIL_ERR_OOM = 5
 ANVIL_ERR_HIP = 6
 
+ANVIL_GRAD_F32 = 0
+ANVIL_GRAD_BF16 = 1
+
 # Every symbol include/anvil.h declares, with its ctypes signature (restype, argtypes).
 _vp, _i64, _f, _i, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_size_t
 _d = ctypes.c_double
@@ -43,6 +46,9 @@ SIGNATURES = {
     "anvil_bank_update_ws": (_i, [_vp, _vp, _f, _f, _f, _vp, _vp, _d, _vp, _vp, _f, _vp,
                                   _i64, _i64, _i64, _vp, _sz, _vp]),
     "anvil_equalizer_lanes": (_i64, [_i64, _i64]),
+    "anvil_bank_step_dev": (_i, [_vp, _i, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),
+    "anvil_bank_update_dev": (_i, [_vp, _i, _vp, _vp, _vp, _vp, _d, _vp, _vp, _vp, _i64, _i64,
+                                   _i64, _vp, _sz, _vp]),
     "anvil_bank_step_maps": (_i, [_vp, _vp, _f, _f, _f, _vp, _i, _vp, _i64, _i64, _i64, _vp, _sz,
                                   _vp]),
     "anvil_equalize": (_i, [_vp, _vp, _d, _vp, _i64, _i64, _i64, _vp]),
@@ -180,6 +186,65 @@ def anvil_bank_step_maps(grad, velocity, momentum, fast_beta, fast_weight, maps,
         ctypes.cast(host, ctypes.c_void_p), len(maps), _ptr(out), g, m, n, ws, wsb,
         _stream(stream)))
     return out
+
+
+def _grad_dtype(grad):
+    import torch
+    if grad.dtype == torch.float32:
+        return ANVIL_GRAD_F32
+    if grad.dtype == torch.bfloat16:
+        return ANVIL_GRAD_BF16
+    raise TypeError("grad must be float32 or bfloat16")
+
+
+def anvil_bank_step_dev(grad, velocity, scalars, out, workspace, stream=None):
+    """The bank step with an fp32 or bf16 gradient and device scalars (fp32 [>= 3]: momentum,
+    fast_beta, fast_weight) into fixed buffers; allocates nothing (graph-capturable)."""
+    import torch
+    lib = load()
+    kind = _grad_dtype(grad)
+    _need(grad, "grad", grad.dtype)
+    g, m, n = _gmn(grad)
+    _need(velocity, "velocity", torch.float32, (2, g, m, n))
+    _need(scalars, "scalars", torch.float32)
+    if scalars.numel() < 3:
+        raise ValueError("scalars must hold momentum, fast_beta, fast_weight")
+    _need(out, "out", torch.bfloat16, (g, m, n))
+    _need(workspace, "workspace", torch.uint8)
+    _check("anvil_bank_step_dev", lib.anvil_bank_step_dev(
+        _ptr(grad), kind, _ptr(velocity), _ptr(scalars), _ptr(out), g, m, n, _ptr(workspace),
+        workspace.numel(), _stream(stream)))
+    return out
+
+
+def anvil_bank_update_dev(grad, velocity, scalars, update, lane_energy, beta2, param, mantissa,
+                          eff_lr, workspace, stream=None):
+    """The whole bank update in the page's bank contract: device scalars (fp32 [4]: momentum,
+    fast_beta, fast_weight, eff_wd), fixed buffers, caller workspace; graph-capturable."""
+    import torch
+    lib = load()
+    kind = _grad_dtype(grad)
+    _need(grad, "grad", grad.dtype)
+    g, m, n = _gmn(grad)
+    _need(velocity, "velocity", torch.float32, (2, g, m, n))
+    _need(scalars, "scalars", torch.float32)
+    if scalars.numel() < 4:
+        raise ValueError("scalars must hold momentum, fast_beta, fast_weight, eff_wd")
+    _need(update, "update", torch.bfloat16, (g, m, n))
+    _need(lane_energy, "lane_energy", torch.float32)
+    if lane_energy.numel() != g * equalizer_lanes(m, n):
+        raise ValueError("lane_energy must hold g * lanes values")
+    _need(param, "param", torch.bfloat16, (g, m, n))
+    if mantissa.dtype not in (torch.int16, torch.uint16):
+        raise TypeError("mantissa must be a 16-bit integer tensor")
+    _need(mantissa, "mantissa", mantissa.dtype, (g, m, n))
+    _need(eff_lr, "eff_lr", torch.float32, (g,))
+    _need(workspace, "workspace", torch.uint8)
+    _check("anvil_bank_update_dev", lib.anvil_bank_update_dev(
+        _ptr(grad), kind, _ptr(velocity), _ptr(scalars), _ptr(update), _ptr(lane_energy), beta2,
+        _ptr(param), _ptr(mantissa), _ptr(eff_lr), g, m, n, _ptr(workspace), workspace.numel(),
+        _stream(stream)))
+    return update
 
 
 def anvil_momentum(grad, velocity, momentum, fast_beta, fast_weight, x_out=None, stream=None):

@@ -2,6 +2,7 @@
 // ANVIL bank step (modded-nanogpt anvil.py, `anvil_cascade`).
 #include <hip/hip_runtime.h>
 
+#include <initializer_list>
 #include <map>
 #include <mutex>
 #include <utility>
@@ -96,22 +97,42 @@ Layout layout_for(const Shape& sh) {
   return l;
 }
 
-int check_step_args(const float* grad, float* velocity, uint16_t* out, const Shape& sh) {
+// A caller buffer: its address and the bytes the call touches.
+struct Buf {
+  const void* p;
+  size_t bytes;
+};
+
+// ANVIL_ERR_ALIAS if any two of the (non-null) buffers overlap.
+int check_disjoint(std::initializer_list<Buf> bufs) {
+  for (auto i = bufs.begin(); i != bufs.end(); ++i)
+    for (auto j = i + 1; j != bufs.end(); ++j)
+      if (i->p && j->p && overlap(i->p, i->bytes, j->p, j->bytes)) return ANVIL_ERR_ALIAS;
+  return ANVIL_OK;
+}
+
+// The step's buffers: grad (fp32 or bf16: grad_bytes per element), velocity, out.
+int check_step_args(const void* grad, size_t grad_bytes, float* velocity, uint16_t* out,
+                    const Shape& sh) {
   if (!grad || !velocity || !out) return ANVIL_ERR_INVALID_ARG;
   if (!aligned(grad, 16) || !aligned(velocity, 16) || !aligned(out, 16)) return ANVIL_ERR_MISALIGNED;
   const size_t cnt = static_cast<size_t>(sh.g) * sh.m * sh.n;
-  if (overlap(out, cnt * 2, grad, cnt * 4) || overlap(out, cnt * 2, velocity, cnt * 8) ||
-      overlap(grad, cnt * 4, velocity, cnt * 8))
-    return ANVIL_ERR_ALIAS;
-  return ANVIL_OK;
+  return check_disjoint({{grad, cnt * grad_bytes}, {velocity, cnt * 8}, {out, cnt * 2}});
 }
 
 // The launch sequence: momentum, Gram 0 with trace, normalise, then per map (Gram, poly, apply).
 // The apply ping-pongs between `out` and the workspace copy; X starts in `out` for an even number
 // of maps and in the workspace copy for an odd number, so that the last apply writes `out`.
-int run_step(const float* grad, float* velocity, float momentum, float fast_beta,
-             float fast_weight, uint16_t* out, const Shape& sh, char* ws, hipStream_t stream,
-             const float (*maps)[3] = kAnvilMaps.v, int steps = 6) {
+// The momentum inputs: an fp32 or bf16 gradient and the rail scalars by value or on the device.
+struct MomentumIn {
+  const void* grad;
+  bool grad_bf16;
+  const float* scalars;   // device (momentum, fast_beta, fast_weight), or null: use the values
+  float momentum, fast_beta, fast_weight;
+};
+
+int run_step(const MomentumIn& mi, float* velocity, uint16_t* out, const Shape& sh, char* ws,
+             hipStream_t stream, const float (*maps)[3] = kAnvilMaps.v, int steps = 6) {
   const Layout l = layout_for(sh);
   uint16_t* ping = reinterpret_cast<uint16_t*>(ws + l.ping);
   uint16_t* A = reinterpret_cast<uint16_t*>(ws + l.a);
@@ -123,8 +144,12 @@ int run_step(const float* grad, float* velocity, float momentum, float fast_beta
 
   uint16_t* X = (steps % 2 == 0) ? out : ping;
   uint16_t* Y = (steps % 2 == 0) ? ping : out;
-  hipError_t e = anvil::launch_momentum(grad, velocity, velocity + count, X, count, momentum,
-                                        fast_beta, fast_weight, stream);
+  hipError_t e =
+      mi.scalars != nullptr
+          ? anvil::launch_momentum_dev(mi.grad, mi.grad_bf16, velocity, velocity + count, X, count,
+                                       mi.scalars, stream)
+          : anvil::launch_momentum(static_cast<const float*>(mi.grad), velocity, velocity + count,
+                                   X, count, mi.momentum, mi.fast_beta, mi.fast_weight, stream);
   if (e != hipSuccess) return hip_status(e);
   e = anvil::launch_gram(X, A, partials, sh, stream);
   if (e != hipSuccess) return hip_status(e);
@@ -144,39 +169,45 @@ int run_step(const float* grad, float* velocity, float momentum, float fast_beta
   return ANVIL_OK;
 }
 
-int check_update_args(const float* grad, const float* velocity, const uint16_t* update,
-                      const float* lane_energy, const uint16_t* param, const uint16_t* mantissa,
-                      const float* eff_lr, const Shape& sh) {
+// The update's buffers on top of the step's; scalars (device fp32 [4]) may be null.
+int check_update_args(const void* grad, size_t grad_bytes, const float* velocity,
+                      const uint16_t* update, const float* lane_energy, const uint16_t* param,
+                      const uint16_t* mantissa, const float* eff_lr, const float* scalars,
+                      const Shape& sh) {
   if (!lane_energy || !param || !mantissa || !eff_lr) return ANVIL_ERR_INVALID_ARG;
   if (!aligned(param, 16) || !aligned(mantissa, 16) || !aligned(lane_energy, 4) ||
-      !aligned(eff_lr, 4))
+      !aligned(eff_lr, 4) || !aligned(scalars, 4))
     return ANVIL_ERR_MISALIGNED;
   const size_t cnt = static_cast<size_t>(sh.g) * sh.m * sh.n;
   const size_t lb = static_cast<size_t>(sh.g) * anvil::equalizer_lanes(sh) * 4;
-  const void* bufs[6] = {grad, velocity, update, param, mantissa, lane_energy};
-  const size_t sizes[6] = {cnt * 4, cnt * 8, cnt * 2, cnt * 2, cnt * 2, lb};
-  for (int i = 0; i < 6; ++i)
-    for (int j = i + 1; j < 6; ++j)
-      if (bufs[i] && bufs[j] && overlap(bufs[i], sizes[i], bufs[j], sizes[j])) return ANVIL_ERR_ALIAS;
-  if (overlap(eff_lr, sh.g * 4, param, cnt * 2) || overlap(eff_lr, sh.g * 4, mantissa, cnt * 2) ||
-      overlap(eff_lr, sh.g * 4, lane_energy, lb))
-    return ANVIL_ERR_ALIAS;
-  return ANVIL_OK;
+  return check_disjoint({{grad, cnt * grad_bytes}, {velocity, cnt * 8}, {update, cnt * 2},
+                         {param, cnt * 2}, {mantissa, cnt * 2}, {lane_energy, lb},
+                         {eff_lr, static_cast<size_t>(sh.g) * 4}, {scalars, 16}});
 }
+
+// The parameter side of the update: the equalizer state and the decay's inputs.
+struct UpdateIn {
+  float* lane_energy;
+  double beta2;
+  uint16_t* param;
+  uint16_t* mantissa;
+  float eff_wd;
+  const float* wd_dev;   // device eff_wd, or null: use the value
+  const float* eff_lr;
+};
 
 // The whole bank update: the step (into `update`), then the equalizer and the decay, gated on the
 // slow rail the step has just written.
-int run_update(const float* grad, float* velocity, float momentum, float fast_beta,
-               float fast_weight, uint16_t* update, float* lane_energy, double beta2,
-               uint16_t* param, uint16_t* mantissa, float eff_wd, const float* eff_lr,
+int run_update(const MomentumIn& mi, float* velocity, uint16_t* update, const UpdateIn& ui,
                const Shape& sh, char* ws, hipStream_t stream) {
-  int st = run_step(grad, velocity, momentum, fast_beta, fast_weight, update, sh, ws, stream);
+  int st = run_step(mi, velocity, update, sh, ws, stream);
   if (st != ANVIL_OK) return st;
   const Layout l = layout_for(sh);
   const int64_t count = sh.g * sh.m * sh.n;
-  return hip_status(anvil::launch_equalize(update, lane_energy, beta2,
+  return hip_status(anvil::launch_equalize(update, ui.lane_energy, ui.beta2,
                                            reinterpret_cast<float*>(ws + l.lanes), sh, stream,
-                                           param, mantissa, velocity + count, eff_lr, eff_wd));
+                                           ui.param, ui.mantissa, velocity + count, ui.eff_lr,
+                                           ui.eff_wd, ui.wd_dev));
 }
 
 // Workspace cache of the allocating entry point, one grow-only buffer per (device, stream).
@@ -210,19 +241,35 @@ int cached_workspace(size_t need, hipStream_t hs, char** out) {
   return ANVIL_OK;
 }
 
-// Checks of a caller-owned workspace against the step's buffers.
-int check_workspace(const void* workspace, size_t workspace_bytes, const float* grad,
-                    const float* velocity, const uint16_t* out, const Shape& sh) {
+// Checks of a caller-owned workspace: size, alignment, and no overlap with the call's buffers.
+int check_workspace(const void* workspace, size_t workspace_bytes, const Shape& sh,
+                    std::initializer_list<Buf> bufs) {
   if (!workspace) return ANVIL_ERR_INVALID_ARG;
   if (!aligned(workspace, kAlign)) return ANVIL_ERR_MISALIGNED;
   const Layout l = layout_for(sh);
   if (workspace_bytes < l.total) return ANVIL_ERR_UNSUPPORTED;
-  const size_t cnt = static_cast<size_t>(sh.g) * sh.m * sh.n;
-  if (overlap(workspace, l.total, grad, cnt * 4) || overlap(workspace, l.total, velocity, cnt * 8) ||
-      overlap(workspace, l.total, out, cnt * 2))
-    return ANVIL_ERR_ALIAS;
+  for (const Buf& b : bufs)
+    if (b.p && overlap(workspace, l.total, b.p, b.bytes)) return ANVIL_ERR_ALIAS;
   return ANVIL_OK;
 }
+
+// The workspace to use: the caller's (checked against `bufs`) or, when null, the cached one.
+int pick_workspace(void* workspace, size_t workspace_bytes, const Shape& sh, hipStream_t hs,
+                   std::initializer_list<Buf> bufs, char** ws) {
+  if (workspace) {
+    const int st = check_workspace(workspace, workspace_bytes, sh, bufs);
+    if (st != ANVIL_OK) return st;
+    *ws = static_cast<char*>(workspace);
+    return ANVIL_OK;
+  }
+  return cached_workspace(layout_for(sh).total, hs, ws);
+}
+
+MomentumIn by_value(const float* grad, float momentum, float fast_beta, float fast_weight) {
+  return MomentumIn{grad, false, nullptr, momentum, fast_beta, fast_weight};
+}
+
+size_t grad_elem_bytes(int grad_dtype) { return grad_dtype == ANVIL_GRAD_BF16 ? 2 : 4; }
 
 }  // namespace
 
@@ -260,12 +307,16 @@ int anvil_bank_step_ws(const float* grad, float* velocity, float momentum, float
   bool empty = false;
   int st = check_shape(g, m, n, &sh, &empty);
   if (st != ANVIL_OK || empty) return st;
-  st = check_step_args(grad, velocity, out, sh);
+  st = check_step_args(grad, 4, velocity, out, sh);
   if (st != ANVIL_OK) return st;
-  st = check_workspace(workspace, workspace_bytes, grad, velocity, out, sh);
+  if (!workspace) return ANVIL_ERR_INVALID_ARG;
+  const size_t cnt = static_cast<size_t>(sh.g) * sh.m * sh.n;
+  char* ws = nullptr;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  st = pick_workspace(workspace, workspace_bytes, sh, hs,
+                      {{grad, cnt * 4}, {velocity, cnt * 8}, {out, cnt * 2}}, &ws);
   if (st != ANVIL_OK) return st;
-  return run_step(grad, velocity, momentum, fast_beta, fast_weight, out, sh,
-                  static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+  return run_step(by_value(grad, momentum, fast_beta, fast_weight), velocity, out, sh, ws, hs);
 }
 
 int anvil_bank_step(const float* grad, float* velocity, float momentum, float fast_beta,
@@ -275,13 +326,13 @@ int anvil_bank_step(const float* grad, float* velocity, float momentum, float fa
   bool empty = false;
   int st = check_shape(g, m, n, &sh, &empty);
   if (st != ANVIL_OK || empty) return st;
-  st = check_step_args(grad, velocity, out, sh);
+  st = check_step_args(grad, 4, velocity, out, sh);
   if (st != ANVIL_OK) return st;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   char* ws = nullptr;
   st = cached_workspace(layout_for(sh).total, hs, &ws);
   if (st != ANVIL_OK) return st;
-  return run_step(grad, velocity, momentum, fast_beta, fast_weight, out, sh, ws, hs);
+  return run_step(by_value(grad, momentum, fast_beta, fast_weight), velocity, out, sh, ws, hs);
 }
 
 int anvil_bank_step_maps(const float* grad, float* velocity, float momentum, float fast_beta,
@@ -294,42 +345,53 @@ int anvil_bank_step_maps(const float* grad, float* velocity, float momentum, flo
   int st = check_shape(g, m, n, &sh, &empty);
   if (st != ANVIL_OK || empty) return st;
   if (!maps) return ANVIL_ERR_INVALID_ARG;
-  st = check_step_args(grad, velocity, out, sh);
+  st = check_step_args(grad, 4, velocity, out, sh);
   if (st != ANVIL_OK) return st;
   hipStream_t hs = static_cast<hipStream_t>(stream);
+  const size_t cnt = static_cast<size_t>(sh.g) * sh.m * sh.n;
   char* ws = nullptr;
-  if (workspace) {
-    st = check_workspace(workspace, workspace_bytes, grad, velocity, out, sh);
-    if (st != ANVIL_OK) return st;
-    ws = static_cast<char*>(workspace);
-  } else {
-    st = cached_workspace(layout_for(sh).total, hs, &ws);
-    if (st != ANVIL_OK) return st;
-  }
+  st = pick_workspace(workspace, workspace_bytes, sh, hs,
+                      {{grad, cnt * 4}, {velocity, cnt * 8}, {out, cnt * 2}}, &ws);
+  if (st != ANVIL_OK) return st;
   float table[kMaxMaps][3];
   for (int k = 0; k < steps; ++k)
     for (int j = 0; j < 3; ++j) table[k][j] = maps[3 * k + j];
-  return run_step(grad, velocity, momentum, fast_beta, fast_weight, out, sh, ws, hs, table, steps);
+  return run_step(by_value(grad, momentum, fast_beta, fast_weight), velocity, out, sh, ws, hs,
+                  table, steps);
+}
+
+int anvil_bank_step_dev(const void* grad, int grad_dtype, float* velocity, const float* scalars,
+                        uint16_t* out, int64_t g, int64_t m, int64_t n, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (grad_dtype != ANVIL_GRAD_F32 && grad_dtype != ANVIL_GRAD_BF16) return ANVIL_ERR_INVALID_ARG;
+  Shape sh;
+  bool empty = false;
+  int st = check_shape(g, m, n, &sh, &empty);
+  if (st != ANVIL_OK || empty) return st;
+  const size_t gb = grad_elem_bytes(grad_dtype);
+  st = check_step_args(grad, gb, velocity, out, sh);
+  if (st != ANVIL_OK) return st;
+  if (!scalars || !workspace) return ANVIL_ERR_INVALID_ARG;
+  if (!aligned(scalars, 4)) return ANVIL_ERR_MISALIGNED;
+  const size_t cnt = static_cast<size_t>(sh.g) * sh.m * sh.n;
+  st = check_disjoint({{scalars, 12}, {velocity, cnt * 8}, {out, cnt * 2}});
+  if (st != ANVIL_OK) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  char* ws = nullptr;
+  st = pick_workspace(workspace, workspace_bytes, sh, hs,
+                      {{grad, cnt * gb}, {velocity, cnt * 8}, {out, cnt * 2}, {scalars, 12}}, &ws);
+  if (st != ANVIL_OK) return st;
+  const MomentumIn mi{grad, grad_dtype == ANVIL_GRAD_BF16, scalars, 0.0f, 0.0f, 0.0f};
+  return run_step(mi, velocity, out, sh, ws, hs);
 }
 
 int anvil_bank_update(const float* grad, float* velocity, float momentum, float fast_beta,
                       float fast_weight, uint16_t* update, float* lane_energy, double beta2,
                       uint16_t* param, uint16_t* mantissa, float eff_wd, const float* eff_lr,
                       int64_t g, int64_t m, int64_t n, void* stream) {
-  Shape sh;
-  bool empty = false;
-  int st = check_shape(g, m, n, &sh, &empty);
-  if (st != ANVIL_OK || empty) return st;
-  st = check_step_args(grad, velocity, update, sh);
-  if (st != ANVIL_OK) return st;
-  st = check_update_args(grad, velocity, update, lane_energy, param, mantissa, eff_lr, sh);
-  if (st != ANVIL_OK) return st;
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  char* ws = nullptr;
-  st = cached_workspace(layout_for(sh).total, hs, &ws);
-  if (st != ANVIL_OK) return st;
-  return run_update(grad, velocity, momentum, fast_beta, fast_weight, update, lane_energy, beta2,
-                    param, mantissa, eff_wd, eff_lr, sh, ws, hs);
+  return anvil_bank_update_ws(grad, velocity, momentum, fast_beta, fast_weight, update,
+                              lane_energy, beta2, param, mantissa, eff_wd, eff_lr, g, m, n,
+                              nullptr, 0, stream);
 }
 
 int anvil_bank_update_ws(const float* grad, float* velocity, float momentum, float fast_beta,
@@ -341,21 +403,56 @@ int anvil_bank_update_ws(const float* grad, float* velocity, float momentum, flo
   bool empty = false;
   int st = check_shape(g, m, n, &sh, &empty);
   if (st != ANVIL_OK || empty) return st;
-  st = check_step_args(grad, velocity, update, sh);
+  st = check_step_args(grad, 4, velocity, update, sh);
   if (st != ANVIL_OK) return st;
-  st = check_update_args(grad, velocity, update, lane_energy, param, mantissa, eff_lr, sh);
+  st = check_update_args(grad, 4, velocity, update, lane_energy, param, mantissa, eff_lr, nullptr,
+                         sh);
   if (st != ANVIL_OK) return st;
-  st = check_workspace(workspace, workspace_bytes, grad, velocity, update, sh);
-  if (st != ANVIL_OK) return st;
-  const Layout l = layout_for(sh);
   const size_t cnt = static_cast<size_t>(sh.g) * sh.m * sh.n;
   const size_t lb = static_cast<size_t>(sh.g) * anvil::equalizer_lanes(sh) * 4;
-  if (overlap(workspace, l.total, param, cnt * 2) || overlap(workspace, l.total, mantissa, cnt * 2) ||
-      overlap(workspace, l.total, lane_energy, lb) || overlap(workspace, l.total, eff_lr, sh.g * 4))
-    return ANVIL_ERR_ALIAS;
-  return run_update(grad, velocity, momentum, fast_beta, fast_weight, update, lane_energy, beta2,
-                    param, mantissa, eff_wd, eff_lr, sh, static_cast<char*>(workspace),
-                    static_cast<hipStream_t>(stream));
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  char* ws = nullptr;
+  st = pick_workspace(workspace, workspace_bytes, sh, hs,
+                      {{grad, cnt * 4}, {velocity, cnt * 8}, {update, cnt * 2}, {param, cnt * 2},
+                       {mantissa, cnt * 2}, {lane_energy, lb},
+                       {eff_lr, static_cast<size_t>(sh.g) * 4}},
+                      &ws);
+  if (st != ANVIL_OK) return st;
+  const UpdateIn ui{lane_energy, beta2, param, mantissa, eff_wd, nullptr, eff_lr};
+  return run_update(by_value(grad, momentum, fast_beta, fast_weight), velocity, update, ui, sh, ws,
+                    hs);
+}
+
+int anvil_bank_update_dev(const void* grad, int grad_dtype, float* velocity,
+                          const float* scalars, uint16_t* update, float* lane_energy,
+                          double beta2, uint16_t* param, uint16_t* mantissa,
+                          const float* eff_lr, int64_t g, int64_t m, int64_t n, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (grad_dtype != ANVIL_GRAD_F32 && grad_dtype != ANVIL_GRAD_BF16) return ANVIL_ERR_INVALID_ARG;
+  Shape sh;
+  bool empty = false;
+  int st = check_shape(g, m, n, &sh, &empty);
+  if (st != ANVIL_OK || empty) return st;
+  const size_t gb = grad_elem_bytes(grad_dtype);
+  st = check_step_args(grad, gb, velocity, update, sh);
+  if (st != ANVIL_OK) return st;
+  if (!scalars || !workspace) return ANVIL_ERR_INVALID_ARG;
+  st = check_update_args(grad, gb, velocity, update, lane_energy, param, mantissa, eff_lr, scalars,
+                         sh);
+  if (st != ANVIL_OK) return st;
+  const size_t cnt = static_cast<size_t>(sh.g) * sh.m * sh.n;
+  const size_t lb = static_cast<size_t>(sh.g) * anvil::equalizer_lanes(sh) * 4;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  char* ws = nullptr;
+  st = pick_workspace(workspace, workspace_bytes, sh, hs,
+                      {{grad, cnt * gb}, {velocity, cnt * 8}, {update, cnt * 2}, {param, cnt * 2},
+                       {mantissa, cnt * 2}, {lane_energy, lb},
+                       {eff_lr, static_cast<size_t>(sh.g) * 4}, {scalars, 16}},
+                      &ws);
+  if (st != ANVIL_OK) return st;
+  const MomentumIn mi{grad, grad_dtype == ANVIL_GRAD_BF16, scalars, 0.0f, 0.0f, 0.0f};
+  const UpdateIn ui{lane_energy, beta2, param, mantissa, 0.0f, scalars + 3, eff_lr};
+  return run_update(mi, velocity, update, ui, sh, ws, hs);
 }
 
 int64_t anvil_equalizer_lanes(int64_t m, int64_t n) {
@@ -431,7 +528,7 @@ int anvil_momentum(const float* grad, float* velocity, float momentum, float fas
   bool empty = false;
   int st = check_shape(g, m, n, &sh, &empty);
   if (st != ANVIL_OK || empty) return st;
-  st = check_step_args(grad, velocity, x_out, sh);
+  st = check_step_args(grad, 4, velocity, x_out, sh);
   if (st != ANVIL_OK) return st;
   const int64_t count = sh.g * sh.m * sh.n;
   return hip_status(anvil::launch_momentum(grad, velocity, velocity + count, x_out, count,

@@ -11,6 +11,12 @@ namespace anvil {
 hipError_t launch_momentum(const float* grad, float* v0, float* v1, uint16_t* x, int64_t count,
                            float momentum, float fast_beta, float fast_weight, hipStream_t stream);
 
+// The same with the gradient fp32 or bf16 and (momentum, fast_beta, fast_weight) read from a
+// device array when the kernel runs.
+hipError_t launch_momentum_dev(const void* grad, bool grad_bf16, float* v0, float* v1,
+                               uint16_t* x, int64_t count, const float* scalars,
+                               hipStream_t stream);
+
 // Geometry of one bank: stack g of m x n matrices.
 struct Shape {
   int64_t g;
@@ -37,10 +43,12 @@ int equalizer_lanes(const Shape& sh);
 
 // Equalizer on u (in place) with lane energies updated in place; scratch holds 2*g*lanes fp32.
 // If param is not null, the same elementwise pass applies the sign-aligned decay to
-// (param, mantissa) with the rescaled u, gate (the slow rail), per-matrix lr and wd.
+// (param, mantissa) with the rescaled u, gate (the slow rail), per-matrix lr and wd (or wd read
+// from the device at *wd_dev when that is not null).
 hipError_t launch_equalize(uint16_t* u, float* lane_energy, double beta2, float* scratch,
                            const Shape& sh, hipStream_t stream, uint16_t* param,
-                           uint16_t* mantissa, const float* gate, const float* lr, float wd);
+                           uint16_t* mantissa, const float* gate, const float* lr, float wd,
+                           const float* wd_dev = nullptr);
 
 // The sign-aligned decay alone, with u as given.
 hipError_t launch_decay(uint16_t* param, uint16_t* mantissa, const uint16_t* u, float wd,

@@ -8,10 +8,13 @@
 //   y = g + mu * (blend - g)            mu = momentum
 //   x = bf16(y)                         round to nearest even
 //
-// HBM-bound: each element reads grad (4 B) and both rails (8 B) and writes both rails (8 B) and
-// x (2 B) — 22 bytes, touched once.  Each thread moves groups of 4 elements with 16-byte loads
-// and stores (8-byte for x), several groups per iteration with all loads issued first; grad and
-// the rails stream through with non-temporal accesses, x stays cacheable for the Gram after it.
+// HBM-bound: each element reads grad (4 B, or 2 B for a bf16 gradient, which the page widens to
+// fp32 exactly before the lerps) and both rails (8 B) and writes both rails (8 B) and x (2 B) —
+// 22 (20) bytes, touched once.  Each thread moves groups of 4 elements with 16-byte loads and
+// stores (8-byte for x and a bf16 grad), several groups per iteration with all loads issued
+// first; grad and the rails stream through with non-temporal accesses, x stays cacheable for the
+// Gram after it.  The rail scalars come by value, or from a device array read when the kernel
+// runs (so a captured graph picks up their current values).
 #include "device_common.h"
 #include "launchers.h"
 
@@ -27,20 +30,47 @@ __device__ __forceinline__ float lerp_doc(float start, float end, float weight) 
   return start + weight * (end - start);
 }
 
+// The rail weights from the fp32 scalars (momentum, fast_beta, fast_weight): 1 - fast_beta and
+// 1 - fast_weight are fp32 subtractions; the slow weight is the host double 1 - 0.98 taken as
+// fp32 (0.02f).
+__host__ __device__ __forceinline__ RailWeights rail_weights(float momentum, float fast_beta,
+                                                             float fast_weight) {
+  RailWeights rw;
+  rw.wf = 1.0f - fast_beta;
+  rw.ws = static_cast<float>(1.0 - 0.98);
+  rw.w = fast_weight;
+  rw.omw = 1.0f - fast_weight;
+  rw.mu = momentum;
+  return rw;
+}
+
 // Groups of 4 elements per thread per iteration, and workgroups per CU of the grid (grid-stride
 // beyond); chosen by measurement on MI355X (about 5.2 TB/s on the 24x2816x768 bank).
 constexpr int kUnroll = 4;
 constexpr int kBlocksPerCu = 16;
 
+// 4 gradient values as fp32: a 16-byte fp32 load, or an 8-byte bf16 load widened exactly.
+__device__ __forceinline__ f32x4_t load_grad4(const float* grad, int64_t i) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(grad) + i);
+}
+__device__ __forceinline__ f32x4_t load_grad4(const uint16_t* grad, int64_t i) {
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(grad) + i);
+  return f32x4_t{bf16_to_f32(v[0] & 0xFFFFu), bf16_to_f32(v[0] >> 16),
+                 bf16_to_f32(v[1] & 0xFFFFu), bf16_to_f32(v[1] >> 16)};
+}
+
 // Each thread moves UNROLL groups of 4 elements per iteration: all loads first (3*UNROLL
-// 16-byte loads in flight), then the arithmetic, then the stores.  A block covers
-// UNROLL*256 consecutive groups, so every load and store instruction stays coalesced.
-template <int UNROLL>
-__global__ __launch_bounds__(256) void momentum_kernel(const f32x4_t* __restrict__ grad,
+// loads in flight), then the arithmetic, then the stores.  A block covers UNROLL*256
+// consecutive groups, so every load and store instruction stays coalesced.  `scalars`, when not
+// null, holds (momentum, fast_beta, fast_weight) on the device and replaces `rw`.
+template <int UNROLL, typename GradT>
+__global__ __launch_bounds__(256) void momentum_kernel(const GradT* __restrict__ grad,
                                                        f32x4_t* __restrict__ v0,
                                                        f32x4_t* __restrict__ v1,
                                                        u32x2_t* __restrict__ x, int64_t n4,
-                                                       RailWeights rw) {
+                                                       RailWeights rw,
+                                                       const float* __restrict__ scalars) {
+  if (scalars != nullptr) rw = rail_weights(scalars[0], scalars[1], scalars[2]);
   const int64_t chunk = (int64_t)UNROLL * blockDim.x;
   const int64_t stride = chunk * gridDim.x;
   for (int64_t base = (int64_t)blockIdx.x * chunk + threadIdx.x; base < n4; base += stride) {
@@ -49,7 +79,7 @@ __global__ __launch_bounds__(256) void momentum_kernel(const f32x4_t* __restrict
     for (int u = 0; u < UNROLL; ++u) {
       const int64_t i = base + (int64_t)u * blockDim.x;
       if (i < n4) {
-        g[u] = __builtin_nontemporal_load(grad + i);
+        g[u] = load_grad4(grad, i);
         a[u] = v0[i];
         c[u] = v1[i];
       }
@@ -77,28 +107,39 @@ __global__ __launch_bounds__(256) void momentum_kernel(const f32x4_t* __restrict
   }
 }
 
-}  // namespace
-
-hipError_t launch_momentum(const float* grad, float* v0, float* v1, uint16_t* x, int64_t count,
-                           float momentum, float fast_beta, float fast_weight,
-                           hipStream_t stream) {
-  RailWeights rw;
-  rw.wf = 1.0f - fast_beta;                 // fp32 subtraction, as on an fp32 device scalar
-  rw.ws = static_cast<float>(1.0 - 0.98);   // host double constant taken as fp32 (0.02f)
-  rw.w = fast_weight;
-  rw.omw = 1.0f - fast_weight;
-  rw.mu = momentum;
+template <typename GradT>
+hipError_t launch_momentum_t(const GradT* grad, float* v0, float* v1, uint16_t* x, int64_t count,
+                             RailWeights rw, const float* scalars, hipStream_t stream) {
   const int64_t n4 = count / 4;
   const int threads = 256;
   int64_t blocks = (n4 + threads * kUnroll - 1) / (threads * kUnroll);
   const int64_t max_blocks = 256 * kBlocksPerCu;
   if (blocks > max_blocks) blocks = max_blocks;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(momentum_kernel<kUnroll>, dim3((unsigned)blocks), dim3(threads), 0,
-                     stream,
-                     reinterpret_cast<const f32x4_t*>(grad), reinterpret_cast<f32x4_t*>(v0),
-                     reinterpret_cast<f32x4_t*>(v1), reinterpret_cast<u32x2_t*>(x), n4, rw);
+  hipLaunchKernelGGL((momentum_kernel<kUnroll, GradT>), dim3((unsigned)blocks), dim3(threads), 0,
+                     stream, grad, reinterpret_cast<f32x4_t*>(v0), reinterpret_cast<f32x4_t*>(v1),
+                     reinterpret_cast<u32x2_t*>(x), n4, rw, scalars);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_momentum(const float* grad, float* v0, float* v1, uint16_t* x, int64_t count,
+                           float momentum, float fast_beta, float fast_weight,
+                           hipStream_t stream) {
+  return launch_momentum_t(grad, v0, v1, x, count, rail_weights(momentum, fast_beta, fast_weight),
+                           nullptr, stream);
+}
+
+hipError_t launch_momentum_dev(const void* grad, bool grad_bf16, float* v0, float* v1,
+                               uint16_t* x, int64_t count, const float* scalars,
+                               hipStream_t stream) {
+  const RailWeights unused = rail_weights(0.0f, 0.0f, 0.0f);
+  if (grad_bf16)
+    return launch_momentum_t(static_cast<const uint16_t*>(grad), v0, v1, x, count, unused,
+                             scalars, stream);
+  return launch_momentum_t(static_cast<const float*>(grad), v0, v1, x, count, unused, scalars,
+                           stream);
 }
 
 }  // namespace anvil

@@ -158,6 +158,7 @@ struct DecayArgs {
   const float* gate;      // the slow rail
   const float* lr;        // per matrix
   float wd;
+  const float* wd_dev;    // when not null, wd is read from here when the kernel runs
 };
 
 // Elementwise: u <- bf16(u * scale[lane]) (if scale), write u back (if write_u), then the decay
@@ -196,6 +197,7 @@ __global__ __launch_bounds__(kThreads) void scale_decay(uint16_t* __restrict__ u
       }
     }
     if (d.param != nullptr) {
+      const float wd = d.wd_dev != nullptr ? *d.wd_dev : d.wd;
       const u32x4_t pv = *reinterpret_cast<const u32x4_t*>(d.param + off);
       const u32x4_t mv = *reinterpret_cast<const u32x4_t*>(d.mantissa + off);
       const f32x4_t g0 = *reinterpret_cast<const f32x4_t*>(d.gate + off);
@@ -209,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void scale_decay(uint16_t* __restrict__ u
         const uint32_t mb = (e & 1) ? (mv[e >> 1] >> 16) : (mv[e >> 1] & 0xFFFFu);
         const float master = __uint_as_float((pb << 16) | mb);
         const float aligned = (gate[e] * master >= 0.0f) ? 1.0f : 0.0f;
-        const float t1 = ((master * aligned) * d.wd) * lr;
+        const float t1 = ((master * aligned) * wd) * lr;
         const float t2 = x[e] * lr;
         const uint32_t raw = __float_as_uint((master - t1) - t2);
         const uint32_t hi = raw >> 16;
@@ -240,7 +242,8 @@ int equalizer_lanes(const Shape& sh) { return sh.m >= sh.n ? sh.m : sh.n; }
 
 hipError_t launch_equalize(uint16_t* u, float* lane_energy, double beta2, float* scratch,
                            const Shape& sh, hipStream_t stream, uint16_t* param,
-                           uint16_t* mantissa, const float* gate, const float* lr, float wd) {
+                           uint16_t* mantissa, const float* gate, const float* lr, float wd,
+                           const float* wd_dev) {
   const bool rows = sh.m >= sh.n;
   const int lanes = equalizer_lanes(sh);
   const int len = rows ? sh.n : sh.m;
@@ -261,7 +264,7 @@ hipError_t launch_equalize(uint16_t* u, float* lane_energy, double beta2, float*
                      lane_energy, scale, lanes, len, w_ema);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  DecayArgs d{param, mantissa, gate, lr, wd};
+  DecayArgs d{param, mantissa, gate, lr, wd, wd_dev};
   const int64_t cpm = (int64_t)sh.m * sh.n / 8;
   hipLaunchKernelGGL(scale_decay, dim3((unsigned)elementwise_blocks(cpm * sh.g)), dim3(kThreads),
                      0, stream, u, scale, true, d, sh.m, sh.n, rows, cpm, sh.g);
@@ -270,7 +273,7 @@ hipError_t launch_equalize(uint16_t* u, float* lane_energy, double beta2, float*
 
 hipError_t launch_decay(uint16_t* param, uint16_t* mantissa, const uint16_t* u, float wd,
                         const float* lr, const float* gate, const Shape& sh, hipStream_t stream) {
-  DecayArgs d{param, mantissa, gate, lr, wd};
+  DecayArgs d{param, mantissa, gate, lr, wd, nullptr};
   const int64_t cpm = (int64_t)sh.m * sh.n / 8;
   hipLaunchKernelGGL(scale_decay, dim3((unsigned)elementwise_blocks(cpm * sh.g)), dim3(kThreads),
                      0, stream, const_cast<uint16_t*>(u), nullptr, false, d, sh.m, sh.n,

@@ -195,3 +195,29 @@ def test_map_table_entry_point_checks(lib):
         anvil.ANVIL_ERR_UNSUPPORTED
     assert lib.anvil_bank_step_maps(*args, tp, 2, C, 2, 64, 32, W + 32, need, None) == \
         anvil.ANVIL_ERR_MISALIGNED
+
+
+def test_device_scalar_entry_points_checks(lib):
+    need = lib.anvil_workspace_bytes(2, 64, 32)
+    S = 0x90000000
+    assert lib.anvil_bank_step_dev(A, 2, B, S, C, 2, 64, 32, W, need, None) == \
+        anvil.ANVIL_ERR_INVALID_ARG                       # bad grad dtype
+    assert lib.anvil_bank_step_dev(A, 1, B, None, C, 2, 64, 32, W, need, None) == \
+        anvil.ANVIL_ERR_INVALID_ARG                       # no scalars
+    assert lib.anvil_bank_step_dev(A, 1, B, S, C, 2, 64, 32, None, 0, None) == \
+        anvil.ANVIL_ERR_INVALID_ARG                       # the workspace is required
+    assert lib.anvil_bank_step_dev(A, 1, B, S + 2, C, 2, 64, 32, W, need, None) == \
+        anvil.ANVIL_ERR_MISALIGNED
+    assert lib.anvil_bank_step_dev(A, 1, B, C + 8, C, 2, 64, 32, W, need, None) == \
+        anvil.ANVIL_ERR_ALIAS                             # scalars inside out
+    # a bf16 gradient is half the bytes: `out` right after it passes the overlap checks (and the
+    # call then stops at the too-small workspace); with an fp32 gradient it overlaps
+    after = A + 2 * 64 * 32 * 2
+    assert lib.anvil_bank_step_dev(A, 1, B, S, after, 2, 64, 32, W, need - 1, None) == \
+        anvil.ANVIL_ERR_UNSUPPORTED
+    assert lib.anvil_bank_step_ws(A, B, 0.95, 0.85, 1.0, after, 2, 64, 32, W, need - 1, None) == \
+        anvil.ANVIL_ERR_ALIAS
+    args = (A, 1, B, S, C, D, 0.95, E, F, L, 2, 64, 32)
+    assert lib.anvil_bank_update_dev(*args, W, need - 1, None) == anvil.ANVIL_ERR_UNSUPPORTED
+    assert lib.anvil_bank_update_dev(A, 1, B, E + 8, C, D, 0.95, E, F, L, 2, 64, 32, W, need,
+                                     None) == anvil.ANVIL_ERR_ALIAS
