@@ -32,10 +32,11 @@
 //    swizzled by k; an MFMA operand is two ds_read_b64_tr_b16, the LDS transpose read: within a
 //    16-lane group, lanes 4j..4j+3 point at 16 consecutive rows of k-row j and lane r receives
 //    the 4 k-values of row r.  No VALU transposes.
-//  * Each wave owns a (BM/WM) x (BN/WN) block of 32x32 MFMA fragments.  Each 64-deep slab is
-//    accumulated into fresh registers and then added to the running sums with IEEE fp32 adds
-//    (the MFMA's own addition into a large running sum roughly doubles the drift from an fp64
-//    reference on low-rank-dominated inputs).
+//  * Each wave owns a (BM/WM) x (BN/WN) block of 32x32 MFMA fragments.  In the Gram, each group
+//    of 8 slabs (512 k) is accumulated into fresh registers and then added to the running sums
+//    with IEEE fp32 adds (one MFMA accumulation chain over thousands of k drifts from an fp64
+//    reference noticeably more than sgemm on low-rank-dominated inputs); the polynomial and the
+//    apply (K = the short side) accumulate directly.
 //  * Tiles are ordered so that consecutive tiles of one matrix land on the same XCD (hardware
 //    dispatches workgroups round-robin over the 8 XCDs, each with its own L2).
 //  * The epilogue goes through LDS, 32 rows at a time per wave: rows leave as 16-byte stores, and
@@ -255,7 +256,7 @@ struct Cfg {
   static_assert(kLoadsPerSlab * (STAGES - 2) < 64, "vmcnt range");
 };
 
-template <int OP, bool PT, bool QT, int BM, int BN, int WM, int WN, int STAGES, int BK, bool SLAB>
+template <int OP, bool PT, bool QT, int BM, int BN, int WM, int WN, int STAGES, int BK, int SLAB>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
   using C = Cfg<BM, BN, WM, WN, STAGES, BK>;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -324,6 +325,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
     }
   };
 
+  f32x16_t slab[SLAB > 0 ? C::kFM : 1][SLAB > 0 ? C::kFN : 1];
   for (int kt = 0; kt < KT; ++kt) {
     // slab kt has landed once at most STAGES-2 younger slabs of this wave are still in flight
     if (KT - 1 - kt >= STAGES - 2) {
@@ -347,16 +349,21 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
     const char* tp = smem + (kt % STAGES) * C::kStageBytes;
     const char* tq = tp + C::kQOffset;
 
-    // SLAB: this slab accumulates into fresh registers, added to the running sums afterwards;
-    // otherwise the MFMAs accumulate into the running sums directly.
-    f32x16_t slab[SLAB ? C::kFM : 1][SLAB ? C::kFN : 1];
-    if constexpr (SLAB) {
+    // SLAB > 0: groups of SLAB consecutive slabs accumulate into fresh registers, which are then
+    // added to the running sums (IEEE fp32 adds); SLAB == 0: the MFMAs accumulate into the
+    // running sums directly.
+    const bool group_start = SLAB > 0 && kt % (SLAB > 0 ? SLAB : 1) == 0;
+    const bool group_end = SLAB > 0 && (kt % (SLAB > 0 ? SLAB : 1) == (SLAB > 0 ? SLAB : 1) - 1 ||
+                                        kt == KT - 1);
+    if constexpr (SLAB > 0) {
+      if (group_start) {
 #pragma unroll
-      for (int fm = 0; fm < C::kFM; ++fm)
+        for (int fm = 0; fm < C::kFM; ++fm)
 #pragma unroll
-        for (int fn = 0; fn < C::kFN; ++fn)
+          for (int fn = 0; fn < C::kFN; ++fn)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) slab[fm][fn][r] = 0.0f;
+            for (int r = 0; r < 16; ++r) slab[fm][fn][r] = 0.0f;
+      }
     }
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
@@ -371,7 +378,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
       for (int fm = 0; fm < C::kFM; ++fm)
 #pragma unroll
         for (int fn = 0; fn < C::kFN; ++fn) {
-          if constexpr (SLAB) {
+          if constexpr (SLAB > 0) {
             slab[fm][fn] =
                 __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[fn], fa[fm], slab[fm][fn], 0, 0, 0);
           } else {
@@ -380,11 +387,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
           }
         }
     }
-    if constexpr (SLAB) {
+    if constexpr (SLAB > 0) {
+      if (group_end) {
 #pragma unroll
-      for (int fm = 0; fm < C::kFM; ++fm)
+        for (int fm = 0; fm < C::kFM; ++fm)
 #pragma unroll
-        for (int fn = 0; fn < C::kFN; ++fn) acc[fm][fn] += slab[fm][fn];
+          for (int fn = 0; fn < C::kFN; ++fn) acc[fm][fn] += slab[fm][fn];
+      }
     }
   }
   __syncthreads();   // every wave is done with the operand ring; reuse it for the epilogue
@@ -552,7 +561,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-template <int OP, bool PT, bool QT, int BM, int BN, int WM, int WN, int STAGES, int BK, bool SLAB>
+template <int OP, bool PT, bool QT, int BM, int BN, int WM, int WN, int STAGES, int BK, int SLAB>
 hipError_t launch(GemmParams p, int64_t g, hipStream_t stream) {
   using C = Cfg<BM, BN, WM, WN, STAGES, BK>;
   auto kern = gemm_kernel<OP, PT, QT, BM, BN, WM, WN, STAGES, BK, SLAB>;
@@ -577,6 +586,15 @@ hipError_t launch(GemmParams p, int64_t g, hipStream_t stream) {
 //    otherwise 128x128 tiles (2x2 waves of 64x64, 64-deep slabs, two stages), which keep more
 //    CUs busy on small stacks.
 constexpr int kSymTile = 128;
+// The Gram (K = the long side, up to thousands) sums each group of 8 slabs (512 k) in fresh
+// registers and adds the group sums to the running sums: on low-rank-dominated inputs one long
+// MFMA accumulation chain drifts from an fp64 reference noticeably more than fp32 sgemm does,
+// while groups of 1 to 8 slabs all match sgemm's drift (measured on the warmed mlp bank); 8
+// keeps the extra adds to one per 512 k.
+#ifndef ANVIL_SLAB_GROUP
+#define ANVIL_SLAB_GROUP 8
+#endif
+constexpr int kGramSlabGroup = ANVIL_SLAB_GROUP;
 constexpr int kFullRound = 512;
 
 }  // namespace
@@ -601,8 +619,9 @@ hipError_t launch_gram(const uint16_t* x, uint16_t* a, float* trace_partials, co
   p.trace_slots = gram_trace_slots(s);
   p.tiles_m = p.tiles_n = ceil_div(s, kSymTile);
   p.tiles = p.tiles_m * (p.tiles_m + 1) / 2;
-  if (sh.tall()) return launch<OP_GRAM, true, true, 128, 128, 2, 2, 2, 64, true>(p, sh.g, stream);
-  return launch<OP_GRAM, false, false, 128, 128, 2, 2, 2, 64, true>(p, sh.g, stream);
+  if (sh.tall())
+    return launch<OP_GRAM, true, true, 128, 128, 2, 2, 2, 64, kGramSlabGroup>(p, sh.g, stream);
+  return launch<OP_GRAM, false, false, 128, 128, 2, 2, 2, 64, kGramSlabGroup>(p, sh.g, stream);
 }
 
 hipError_t launch_poly(const uint16_t* a, uint16_t* bout, float coef_b, float coef_c, int64_t g,
@@ -624,7 +643,7 @@ hipError_t launch_poly(const uint16_t* a, uint16_t* bout, float coef_b, float co
   p.beta = coef_c;
   p.tiles_m = p.tiles_n = ceil_div(s, kSymTile);
   p.tiles = p.tiles_m * (p.tiles_m + 1) / 2;
-  return launch<OP_POLY, false, false, 128, 128, 2, 2, 2, 64, false>(p, g, stream);
+  return launch<OP_POLY, false, false, 128, 128, 2, 2, 2, 64, 0>(p, g, stream);
 }
 
 template <int BM, int BN, int WM, int WN, int STAGES, int BK>
@@ -656,7 +675,7 @@ hipError_t launch_apply_cfg(const uint16_t* x, const uint16_t* bm, uint16_t* c, 
     p.bytesQ = (uint32_t)((int64_t)s * s * 2);
     p.ldq = s;
     p.K = sh.n;
-    return launch<OP_APPLY, false, false, BM, BN, WM, WN, STAGES, BK, false>(p, sh.g, stream);
+    return launch<OP_APPLY, false, false, BM, BN, WM, WN, STAGES, BK, 0>(p, sh.g, stream);
   }
   // C = a X + B X: P = rows of B (K = m contiguous), Q(j, k) = X[k][j] (K-major)
   p.P = bm;
@@ -668,7 +687,7 @@ hipError_t launch_apply_cfg(const uint16_t* x, const uint16_t* bm, uint16_t* c, 
   p.bytesQ = (uint32_t)((int64_t)sh.m * sh.n * 2);
   p.ldq = sh.n;
   p.K = sh.m;
-  return launch<OP_APPLY, false, true, BM, BN, WM, WN, STAGES, BK, false>(p, sh.g, stream);
+  return launch<OP_APPLY, false, true, BM, BN, WM, WN, STAGES, BK, 0>(p, sh.g, stream);
 }
 
 hipError_t launch_apply(const uint16_t* x, const uint16_t* bm, uint16_t* c, float coef_a,
