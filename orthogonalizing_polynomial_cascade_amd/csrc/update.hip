@@ -103,7 +103,11 @@ __global__ __launch_bounds__(kThreads) void lane_power_cols(const uint16_t* __re
   }
 }
 
-// Fixed-order block sum of one value per thread (256 threads).
+// One workgroup per matrix for the per-lane terms: 1024 threads, a few lanes each.
+constexpr int kScaleThreads = 1024;
+
+// Fixed-order block sum of one value per thread (kScaleThreads threads): butterfly within each
+// wave, then the wave sums in wave order.
 __device__ float block_sum(float v, float* red) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
@@ -112,17 +116,17 @@ __device__ float block_sum(float v, float* red) {
   __syncthreads();
   float t = 0.0f;
 #pragma unroll
-  for (int w = 0; w < kThreads / 64; ++w) t += red[w];
+  for (int w = 0; w < kScaleThreads / 64; ++w) t += red[w];
   __syncthreads();
   return t;
 }
 
 // One workgroup per matrix: pre and post norms, the energy EMA, the bf16 lane scales.
-__global__ __launch_bounds__(kThreads) void lane_scales(const float* __restrict__ power,
-                                                        float* __restrict__ energy,
-                                                        float* __restrict__ scale, int lanes,
-                                                        int len, float w_ema) {
-  __shared__ float red[kThreads / 64];
+__global__ __launch_bounds__(kScaleThreads) void lane_scales(const float* __restrict__ power,
+                                                             float* __restrict__ energy,
+                                                             float* __restrict__ scale, int lanes,
+                                                             int len, float w_ema) {
+  __shared__ float red[kScaleThreads / 64];
   const int64_t b = blockIdx.x;
   const float* pw = power + b * lanes;
   float* en = energy + b * lanes;
@@ -130,12 +134,12 @@ __global__ __launch_bounds__(kThreads) void lane_scales(const float* __restrict_
   const float flen = static_cast<float>(len);
 
   float ps = 0.0f;
-  for (int l = threadIdx.x; l < lanes; l += kThreads) ps += pw[l];
+  for (int l = threadIdx.x; l < lanes; l += kScaleThreads) ps += pw[l];
   const float psum = block_sum(ps, red);
   const float pre = sqrt_rn(psum * flen);
 
   float qs = 0.0f;
-  for (int l = threadIdx.x; l < lanes; l += kThreads) {
+  for (int l = threadIdx.x; l < lanes; l += kScaleThreads) {
     const float p = pw[l];
     const float e = en[l] + w_ema * (p - en[l]);
     en[l] = e;
@@ -147,7 +151,7 @@ __global__ __launch_bounds__(kThreads) void lane_scales(const float* __restrict_
   }
   const float post = sqrt_rn(block_sum(qs, red));
   const float ratio = pre / fmaxf(post, 1e-10f);
-  for (int l = threadIdx.x; l < lanes; l += kThreads) {
+  for (int l = threadIdx.x; l < lanes; l += kScaleThreads) {
     sc[l] = bf16_to_f32(f32_to_bf16(sc[l] * ratio));
   }
 }
@@ -260,7 +264,7 @@ hipError_t launch_equalize(uint16_t* u, float* lane_energy, double beta2, float*
   if (e != hipSuccess) return e;
   // 1 - beta2 formed in double and taken as fp32, as the page's lerp weight
   const float w_ema = static_cast<float>(1.0 - beta2);
-  hipLaunchKernelGGL(lane_scales, dim3((unsigned)sh.g), dim3(kThreads), 0, stream, power,
+  hipLaunchKernelGGL(lane_scales, dim3((unsigned)sh.g), dim3(kScaleThreads), 0, stream, power,
                      lane_energy, scale, lanes, len, w_ema);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
