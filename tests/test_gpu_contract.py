@@ -128,3 +128,21 @@ def test_graph_capture_replays_match_eager(gpu_lib):
         call(eag, sc_eag, grads[t])
         torch.cuda.synchronize()
         _same(_snapshot(cap), _snapshot(eag))
+
+
+@pytest.mark.parametrize("wname", ["mlp", "us"])
+def test_bf16_gradient_full_size(gpu_lib, wname):
+    """Full stack, benchmark configuration: the bf16-gradient, device-scalar step equals the fp32
+    entry point on the widened gradient bit-exactly (rails and update)."""
+    import torch
+    w = W.ALL[wname]()
+    g, m, n = w.g, w.m, w.n
+    Gw = O.R(w.grad(w.measured[0]))
+    Gb = torch.from_numpy(Gw).cuda().to(torch.bfloat16)
+    mu, fb, fw = gpu_lib.rail_scalars(w.step_ids[w.measured[0]])
+    a, b = _state(gpu_lib, g, m, n), _state(gpu_lib, g, m, n)
+    scal = torch.tensor([mu, fb, fw], dtype=torch.float32, device="cuda")
+    gpu_lib.anvil_bank_step_dev(Gb, a["vel"], scal, a["out"], a["ws"])
+    gpu_lib.anvil_bank_step(to_gpu_f32(Gw), b["vel"], mu, fb, fw, out=b["out"], workspace=b["ws"])
+    assert np.array_equal(bf16_bits_of(a["out"]), bf16_bits_of(b["out"]))
+    assert torch.equal(a["vel"], b["vel"])

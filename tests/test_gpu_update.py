@@ -250,3 +250,43 @@ def test_bank_update_workspace_variant_is_identical(gpu_lib):
                      from_gpu(vel)])
     for a, b in zip(*runs):
         assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("wname", ["mlp", "us", "qk"])
+def test_bank_update_full_size_sampled(gpu_lib, wname):
+    """The whole update on the full stack in the benchmark's configuration (state from the
+    seeded parameter-state generator); the oracle's bank_update on sampled matrices (the
+    equalizer and the decay act per matrix, so a matrix can be checked alone)."""
+    import torch
+    w = W.ALL[wname]()
+    g, m, n = w.g, w.m, w.n
+    st = W.update_state(w)
+    t = w.measured[0]
+    mu, fb, fw = gpu_lib.rail_scalars(w.step_ids[t])
+    G = w.grad(t)
+    vel = torch.zeros((2, g, m, n), dtype=torch.float32, device="cuda")
+    pd, md, ed, lrd = _gpu_tensors(st.param_bits, st.mantissa, st.lane_energy[..., None], st.eff_lr)
+    ws = torch.empty(gpu_lib.workspace_bytes(g, m, n), dtype=torch.uint8, device="cuda")
+    upd = from_gpu(gpu_lib.anvil_bank_update(to_gpu_f32(G), vel, mu, fb, fw, ed, st.beta2, pd, md,
+                                             st.eff_wd, lrd, workspace=ws))
+    p_gpu, m_gpu = bf16_bits_of(pd), md.cpu().numpy().view(np.uint16)
+    e_gpu = from_gpu(ed)
+    lanes = m if m >= n else n
+    for i in sorted({0, 1, g - 1}):
+        e0 = st.lane_energy[i:i + 1].reshape(_lane_shape(1, m, n))
+        u_or, v_or, e_or, p_or, m_or = O.bank_update(
+            G[i:i + 1], np.zeros((2, 1, m, n), np.float32), mu, fb, fw, e0, st.beta2,
+            st.param_bits[i:i + 1], st.mantissa[i:i + 1], st.eff_wd, st.eff_lr[i:i + 1])
+        u_or = O.bf16_to_f32(u_or)[0]
+        r = rel_fro(upd[i], u_or)
+        tol = OUT_TOL
+        if r > OUT_TOL:
+            X = O.R(O.momentum_step(G[i:i + 1], np.zeros((2, 1, m, n), np.float32), mu, fb, fw)[1])
+            tol = max(OUT_TOL, FLOOR_FACTOR * rel_fro(O.cascade(X, acc="fp32")[0], O.cascade(X)[0]))
+        assert r <= tol, f"matrix {i}: update {r:.3e} > {tol:.3e}"
+        assert rel_fro(e_gpu[i], e_or.reshape(lanes)) <= 2 * tol
+        master_old = ((st.param_bits[i].astype(np.uint32) << 16) | st.mantissa[i]).view(np.float32)
+        master_gpu = ((p_gpu[i].astype(np.uint32) << 16) | m_gpu[i]).view(np.float32)
+        master_or = ((p_or[0].astype(np.uint32) << 16) | m_or[0]).view(np.float32)
+        assert rel_fro(master_gpu.astype(np.float64) - master_old,
+                       master_or.astype(np.float64) - master_old) <= 2 * tol
