@@ -274,8 +274,10 @@ def run_workload(anvil, name, steps, warmup, with_stages=True):
         st = time_stages(anvil, w)
         rec["stage_us"] = st
         rec["momentum_gbs"] = momentum_bytes(w.g, w.m, w.n) / (st["momentum"] * 1e-6) / 1e9
+        rec["momentum_pct_hbm"] = 100.0 * rec["momentum_gbs"] / PEAK_HBM_GBS
         for k in ("gram", "poly", "apply"):
             rec[f"{k}_tflops"] = f[k] / 6 / (st[k] * 1e-6) / 1e12
+            rec[f"{k}_pct_bf16_peak"] = 100.0 * rec[f"{k}_tflops"] / PEAK_BF16_TFLOPS
     return w, rec
 
 
