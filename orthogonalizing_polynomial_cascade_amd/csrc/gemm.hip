@@ -143,39 +143,60 @@ __device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t lds, uint32_t voff)
                : "memory", "m0");
 }
 
-// Issue the DMA of one slab of an operand (rows row0.., k0..k0+BK-1) into LDS at `dst`.  The slab
-// is ROWS*BK/512 wave-instructions of 1 KB; instruction u lands at dst + u*1024, lane L's 16 bytes
-// at dst + u*1024 + 16*L.
+// The DMA of one operand's slabs (rows row0.., k0..k0+BK-1) into LDS.  A slab is ROWS*BK/512
+// wave-instructions of 1 KB; instruction u lands at dst + u*1024, lane L's 16 bytes at
+// dst + u*1024 + 16*L, and this wave issues instructions u = wave, wave + NW, ...  The per-lane
+// source offsets of k0 = 0 are computed once per tile; a slab then costs one add per instruction
+// (all destination arithmetic is scalar).  Lanes past the matrix edge get an offset past the
+// buffer's range, which loads zeros.
 template <bool KMAJOR, int ROWS, int BK, int NW>
-__device__ __forceinline__ void issue_slab(i32x4_t rsrc, const char* dst, int ld,
-                                           int row0, int rows, int k0, int K, int wave,
-                                           int lane) {
-  constexpr int kInsts = ROWS * BK / 512;
-  static_assert(kInsts % NW == 0, "slab instructions must split evenly over the waves");
+struct SlabCopy {
+  static constexpr int kInsts = ROWS * BK / 512 / NW;
+  static_assert(ROWS * BK / 512 % NW == 0, "slab instructions must split evenly over the waves");
+  uint32_t vbase[kInsts];   // byte offset at k0 = 0, or kOOB for rows past the edge
+  int kin[kInsts];          // the lane's k offset inside the slab (for the ragged last slab)
+  uint32_t kbytes;          // bytes per unit of k0
+
+  __device__ __forceinline__ SlabCopy(int ld, int row0, int rows, int wave, int lane) {
+    kbytes = KMAJOR ? 2u * (uint32_t)ld : 2u;
 #pragma unroll
-  for (int i = 0; i < kInsts / NW; ++i) {
-    const int u = wave + i * NW;
-    uint32_t voff;
-    if constexpr (!KMAJOR) {
-      constexpr int kSlots = BK / 8;
-      constexpr int kRowsPerInst = 64 / kSlots;
-      const int row = kRowsPerInst * u + lane / kSlots;
-      const int c = (lane % kSlots) ^ ((row / KContig<ROWS, BK>::kRowsPer256) % kSlots);
-      const int gr = row0 + row;
-      const int gk = k0 + c * 8;
-      voff = (gr < rows && gk < K) ? (uint32_t)(gr * ld + gk) * 2u : kOOB;
-    } else {
-      constexpr int kSlots = ROWS / 8;
-      constexpr int kRowsPerKb = 64 / kSlots;
-      const int kr = u * kRowsPerKb + lane / kSlots;
-      const int c = (lane % kSlots) ^ ((kr & 3) << 2);
-      const int gk = k0 + kr;
-      const int gr = row0 + c * 8;
-      voff = (gr < rows && gk < K) ? (uint32_t)(gk * ld + gr) * 2u : kOOB;
+    for (int i = 0; i < kInsts; ++i) {
+      const int u = wave + i * NW;
+      if constexpr (!KMAJOR) {
+        constexpr int kSlots = BK / 8;
+        constexpr int kRowsPerInst = 64 / kSlots;
+        const int row = kRowsPerInst * u + lane / kSlots;
+        const int c = (lane % kSlots) ^ ((row / KContig<ROWS, BK>::kRowsPer256) % kSlots);
+        const int gr = row0 + row;
+        kin[i] = c * 8;
+        vbase[i] = gr < rows ? (uint32_t)(gr * ld + c * 8) * 2u : kOOB;
+      } else {
+        constexpr int kSlots = ROWS / 8;
+        constexpr int kRowsPerKb = 64 / kSlots;
+        const int kr = u * kRowsPerKb + lane / kSlots;
+        const int c = (lane % kSlots) ^ ((kr & 3) << 2);
+        const int gr = row0 + c * 8;
+        kin[i] = kr;
+        vbase[i] = gr < rows ? (uint32_t)(kr * ld + gr) * 2u : kOOB;
+      }
     }
-    dma16(rsrc, lds_addr(dst + u * 1024), voff);
   }
-}
+
+  // Issue this wave's instructions of the slab at k0 into LDS at byte address `dst` (uniform).
+  __device__ __forceinline__ void issue(i32x4_t rsrc, uint32_t dst, int k0, int K, int wave) const {
+    const uint32_t koff = (uint32_t)k0 * kbytes;
+    if (k0 + BK <= K) {
+#pragma unroll
+      for (int i = 0; i < kInsts; ++i)
+        dma16(rsrc, dst + (uint32_t)(wave + i * NW) * 1024u, vbase[i] + koff);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kInsts; ++i)
+        dma16(rsrc, dst + (uint32_t)(wave + i * NW) * 1024u,
+              k0 + kin[i] < K ? vbase[i] + koff : kOOB);
+    }
+  }
+};
 
 // MFMA operand of a 32-row fragment (rows R0..R0+31) at k-step ks (k = 16ks .. 16ks+15):
 // lane l holds row R0 + l%32, k = 16ks + 8(l/32) + 0..7.
@@ -264,7 +285,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN;
   const int wn = wave % WN;
 
@@ -283,6 +304,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
 
   const i32x4_t rP = make_rsrc(p.P + b * p.strideP, p.bytesP);
   const i32x4_t rQ = make_rsrc(p.Q + b * p.strideQ, p.bytesQ);
+  const SlabCopy<PT, BM, BK, C::kWaves> copyP(p.ldp, i0, p.M, wave, lane);
+  const SlabCopy<QT, BN, BK, C::kWaves> copyQ(p.ldq, j0, p.N, wave, lane);
+  const uint32_t smem_lds = lds_addr(smem);
 
   f32x16_t acc[C::kFM][C::kFN];
 #pragma unroll
@@ -298,10 +322,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s) {
     if (s < KT) {
-      char* st = smem + s * C::kStageBytes;
-      issue_slab<PT, BM, BK, C::kWaves>(rP, st, p.ldp, i0, p.M, s * BK, p.K, wave, lane);
-      issue_slab<QT, BN, BK, C::kWaves>(rQ, st + C::kQOffset, p.ldq, j0, p.N, s * BK, p.K, wave,
-                                        lane);
+      const uint32_t st = smem_lds + (uint32_t)(s * C::kStageBytes);
+      copyP.issue(rP, st, s * BK, p.K, wave);
+      copyQ.issue(rQ, st + (uint32_t)C::kQOffset, s * BK, p.K, wave);
     }
   }
 
@@ -337,10 +360,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
     {
       const int kn = kt + STAGES - 1;
       if (kn < KT) {
-        char* st = smem + (kn % STAGES) * C::kStageBytes;
-        issue_slab<PT, BM, BK, C::kWaves>(rP, st, p.ldp, i0, p.M, kn * BK, p.K, wave, lane);
-        issue_slab<QT, BN, BK, C::kWaves>(rQ, st + C::kQOffset, p.ldq, j0, p.N, kn * BK, p.K,
-                                          wave, lane);
+        const uint32_t st = smem_lds + (uint32_t)((kn % STAGES) * C::kStageBytes);
+        copyP.issue(rP, st, kn * BK, p.K, wave);
+        copyQ.issue(rQ, st + (uint32_t)C::kQOffset, kn * BK, p.K, wave);
       }
     }
     if constexpr (kHasE) {
