@@ -80,6 +80,10 @@ def test_unsupported_shapes(lib):
     assert _step(lib, n=30) == anvil.ANVIL_ERR_UNSUPPORTED
     assert _step(lib, g=70000) == anvil.ANVIL_ERR_UNSUPPORTED
     assert _step(lib, m=65536, n=32768) == anvil.ANVIL_ERR_UNSUPPORTED
+    # one matrix may hold at most 2^30 elements (2 GiB of bf16)
+    assert _step(lib, m=32768, n=32776) == anvil.ANVIL_ERR_UNSUPPORTED
+    assert lib.anvil_workspace_bytes(1, 32768, 32768) > 0
+    assert lib.anvil_workspace_bytes(1, 32768, 32776) == 0
     assert lib.anvil_workspace_bytes(1, 60, 32) == 0
     need = lib.anvil_workspace_bytes(2, 64, 32)
     assert _step_ws(lib, wsb=need - 1) == anvil.ANVIL_ERR_UNSUPPORTED
