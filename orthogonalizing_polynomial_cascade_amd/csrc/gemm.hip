@@ -44,6 +44,8 @@
 //    stores.
 //
 // Shapes: M, N, K are multiples of 8 (16-byte rows).
+#include <atomic>
+
 #include "device_common.h"
 #include "launchers.h"
 
@@ -587,12 +589,18 @@ template <int OP, bool PT, bool QT, int BM, int BN, int WM, int WN, int STAGES, 
 hipError_t launch(GemmParams p, int64_t g, hipStream_t stream) {
   using C = Cfg<BM, BN, WM, WN, STAGES, BK>;
   auto kern = gemm_kernel<OP, PT, QT, BM, BN, WM, WN, STAGES, BK, SLAB>;
-  static bool configured = false;   // raise the dynamic LDS limit once per instantiation
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
+  // raise the dynamic LDS limit once per instantiation and device (bit d of the mask: device d;
+  // devices past 63 set it on every launch)
+  static std::atomic<uint64_t> configured{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (uint64_t(1) << dev) : 0;
+  if (bit == 0 || !(configured.load(std::memory_order_acquire) & bit)) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
     if (e != hipSuccess) return e;
-    configured = true;
+    configured.fetch_or(bit, std::memory_order_release);
   }
   p.total = (int)(p.tiles * g);
   hipLaunchKernelGGL(kern, dim3((unsigned)p.total), dim3(C::kThreads), C::kLdsBytes, stream, p);
