@@ -24,8 +24,8 @@
  *     synchronise, and kernel faults surface at the caller's next synchronisation.
  *   - g, m, n: stack size and matrix shape.  Any of them 0 means an empty stack: the call returns
  *     ANVIL_OK without touching memory (pointers may then be NULL).  Negative sizes are
- *     ANVIL_ERR_INVALID_ARG.  m and n must be multiples of 8 (16-byte rows), m*n <= 2^30 and
- *     g <= 65535, else ANVIL_ERR_UNSUPPORTED.
+ *     ANVIL_ERR_INVALID_ARG.  m and n must be multiples of 8 (16-byte rows), m*n <= 2^30,
+ *     g <= 65535 and g*m*n <= 2^35, else ANVIL_ERR_UNSUPPORTED.
  *   - Pointers must be 16-byte aligned (ANVIL_ERR_MISALIGNED).  Outputs may not overlap inputs
  *     (ANVIL_ERR_ALIAS), except where an argument is documented as in-place.
  *   - The caller owns every buffer.  The library owns only the workspaces cached by

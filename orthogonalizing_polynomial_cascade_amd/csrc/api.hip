@@ -63,6 +63,9 @@ int check_shape(int64_t g, int64_t m, int64_t n, Shape* sh, bool* empty) {
   // one bf16 matrix at most 2 GiB: every buffer offset (and the past-the-end offset that loads
   // zeros at ragged edges) stays below 2^32
   if (m * n > (int64_t(1) << 30)) return ANVIL_ERR_UNSUPPORTED;
+  // a whole stack at most 2^35 elements (already 384 GiB of gradient and rails, more than one
+  // GPU holds): every launch grid stays far below 2^31 workgroups
+  if (g * m * n > (int64_t(1) << 35)) return ANVIL_ERR_UNSUPPORTED;
   sh->g = g;
   sh->m = static_cast<int>(m);
   sh->n = static_cast<int>(n);
@@ -282,7 +285,8 @@ const char* anvil_status_string(int status) {
     case ANVIL_OK: return "ok";
     case ANVIL_ERR_INVALID_ARG: return "invalid argument (null pointer, negative size or bad flag)";
     case ANVIL_ERR_UNSUPPORTED:
-      return "unsupported shape (m and n must be multiples of 8, m*n <= 2^30, g <= 65535) or workspace too small";
+      return "unsupported shape (m and n must be multiples of 8, m*n <= 2^30, g <= 65535, "
+             "g*m*n <= 2^35) or workspace too small";
     case ANVIL_ERR_MISALIGNED: return "pointer not 16-byte aligned (workspace: 256-byte)";
     case ANVIL_ERR_ALIAS: return "an output overlaps an input";
     case ANVIL_ERR_OOM: return "workspace allocation failed";

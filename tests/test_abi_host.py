@@ -84,6 +84,10 @@ def test_unsupported_shapes(lib):
     assert _step(lib, m=32768, n=32776) == anvil.ANVIL_ERR_UNSUPPORTED
     assert lib.anvil_workspace_bytes(1, 32768, 32768) > 0
     assert lib.anvil_workspace_bytes(1, 32768, 32776) == 0
+    # whole stack at most 2^35 elements
+    assert lib.anvil_workspace_bytes(32, 32768, 32768) > 0
+    assert lib.anvil_workspace_bytes(33, 32768, 32768) == 0
+    assert lib.anvil_workspace_bytes(65535, 32768, 32768) == 0
     assert lib.anvil_workspace_bytes(1, 60, 32) == 0
     need = lib.anvil_workspace_bytes(2, 64, 32)
     assert _step_ws(lib, wsb=need - 1) == anvil.ANVIL_ERR_UNSUPPORTED
