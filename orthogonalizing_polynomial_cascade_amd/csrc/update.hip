@@ -202,10 +202,14 @@ __global__ __launch_bounds__(kThreads) void scale_decay(uint16_t* __restrict__ u
     }
     if (d.param != nullptr) {
       const float wd = d.wd_dev != nullptr ? *d.wd_dev : d.wd;
-      const u32x4_t pv = *reinterpret_cast<const u32x4_t*>(d.param + off);
-      const u32x4_t mv = *reinterpret_cast<const u32x4_t*>(d.mantissa + off);
-      const f32x4_t g0 = *reinterpret_cast<const f32x4_t*>(d.gate + off);
-      const f32x4_t g1 = *reinterpret_cast<const f32x4_t*>(d.gate + off + 4);
+      // param, mantissa and gate are touched once per step: stream them past the caches
+      const u32x4_t pv =
+          __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(d.param + off));
+      const u32x4_t mv =
+          __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(d.mantissa + off));
+      const f32x4_t g0 = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(d.gate + off));
+      const f32x4_t g1 =
+          __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(d.gate + off + 4));
       const float gate[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
       const float lr = d.lr[b];
       u32x4_t po, mo;
@@ -228,15 +232,15 @@ __global__ __launch_bounds__(kThreads) void scale_decay(uint16_t* __restrict__ u
           mo[e >> 1] = lo;
         }
       }
-      *reinterpret_cast<u32x4_t*>(d.param + off) = po;
-      *reinterpret_cast<u32x4_t*>(d.mantissa + off) = mo;
+      __builtin_nontemporal_store(po, reinterpret_cast<u32x4_t*>(d.param + off));
+      __builtin_nontemporal_store(mo, reinterpret_cast<u32x4_t*>(d.mantissa + off));
     }
   }
 }
 
 int64_t elementwise_blocks(int64_t chunks) {
   int64_t blocks = (chunks + kThreads - 1) / kThreads;
-  const int64_t cap = 256 * 16;
+  const int64_t cap = 256 * 32;   // workgroups per CU: measured on MI355X
   return blocks < 1 ? 1 : (blocks > cap ? cap : blocks);
 }
 
