@@ -294,8 +294,8 @@ def main():
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the ANVIL bank step has no cross-GPU path in this build "
-              "(run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU: the ANVIL bank step runs on a single GPU and has no "
+              "cross-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     import torch

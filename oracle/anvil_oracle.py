@@ -16,7 +16,7 @@ What it computes (source: modded-nanogpt, `track_1_short/optim/anvil.py`, functi
   4. six quintic maps: B = b*A + c*A@A, then X <- a*X + X@B (tall) or a*X + B@X (wide), with the
      Gram recomputed from the current X for every map after the first.
 
-Precision model (the plainest reading of the page; each point is listed in the design doc):
+Precision model (the plainest reading of the page where it leaves the precision open):
   * elementwise steps are fp32 operations, each rounded separately (numpy float32 arithmetic,
     no fused multiply-add);
   * every matrix product is taken in fp64 from the bf16 operands, rounded once to fp32 (the
