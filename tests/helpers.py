@@ -61,3 +61,22 @@ def oracle_normalised_pair(rng, g, m, n):
     A = O.gram(X, tall)
     _, d = O.trace_scale(A)
     return O.normalize(X, A, d)
+
+
+def sigma_classes(s):
+    """Counts (c1, c2, c3) of the values 1, 1/2, 1/4 on the diagonal of the large matrix and a
+    number r of filler values 16 for a 64x64 diagonal stand-in, with equal traces:
+    c1 + c2/4 + c3/16 = 1 + 1/4 + 1/16 + 256 r.  Every square and partial sum is exact in fp32,
+    so both traces (and d) are the same whatever the summation order.  The most even split."""
+    best = None
+    for r in range(1, 62):
+        rhs = 21 + 4096 * r - s          # 15 c1 + 3 c2 = 16 * trace - s
+        if rhs < 0 or rhs % 3:
+            continue
+        k = rhs // 3                     # 5 c1 + c2 = k, c1 + c2 <= s
+        for c1 in range(max(0, -(-(k - s) // 4)), k // 5 + 1):
+            c2 = k - 5 * c1
+            c3 = s - c1 - c2
+            if c2 >= 0 and c3 >= 0 and (best is None or min(c1, c2, c3) > min(best[1])):
+                best = (r, (c1, c2, c3))
+    return best

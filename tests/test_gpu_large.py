@@ -8,7 +8,7 @@ import pytest
 
 from oracle import anvil_oracle as O
 from orthogonalizing_polynomial_cascade_amd import workloads as W
-from tests.helpers import from_gpu, to_gpu_f32
+from tests.helpers import from_gpu, sigma_classes, to_gpu_f32
 
 pytestmark = pytest.mark.gpu
 
@@ -35,3 +35,56 @@ def test_large_ragged_matrix(gpu_lib, m, n):
     assert sv.min() > 0.7 and sv.max() < 1.3, (sv.min(), sv.max())
     assert sv.min() > 0.9 and sv.max() < 1.1, (sv.min(), sv.max())
     assert torch.isfinite(o).all()
+
+
+
+@pytest.mark.parametrize("m,n", [(32768, 32768), (65536, 16384), (16384, 65536)])
+def test_max_size_permuted_diagonal(gpu_lib, m, n):
+    """One matrix of exactly 2^30 elements (the largest supported: 2 GiB of bf16 per buffer) whose
+    nonzeros form a permuted diagonal of powers of two.  Every product in the cascade then has at
+    most one nonzero term, so it is exact in any summation order, and the update must be the same
+    permutation of the cascade of the bare diagonal, bit for bit: the oracle's cascade of a 64x64
+    diagonal with the same trace gives those values (split rounding, as for more than 1024 rows).
+    Checked for the six maps and, through the map-table entry point, for the first two (where the
+    three values are still apart, so a value paired with the wrong line would show).  The rails
+    are set to the gradient and fast_weight is 1, so the lookahead is the gradient."""
+    import torch
+    s = min(m, n)
+    r, counts = sigma_classes(s)
+    classes = np.array([1.0, 0.5, 0.25], np.float32)
+    diag = np.zeros(64, np.float32)
+    diag[:3] = classes
+    diag[3:3 + r] = 16.0
+    want = {}
+    for k in (6, 2):      # the six maps, and the first two (whose three values are still apart)
+        small = O.cascade(np.diag(diag)[None], split=True, maps=O.ANVIL_MAPS[:k])[0]
+        assert np.count_nonzero(small) == 3 + r
+        want[k] = np.array([small[i, i] for i in range(3)], np.float32)
+    assert len(set(want[2].tolist())) == 3
+
+    gen = torch.Generator().manual_seed(m + 3 * n)
+    cls = torch.cat([torch.full((c,), i, dtype=torch.int64) for i, c in enumerate(counts)])
+    cls = cls[torch.randperm(s, generator=gen)]
+    lines = torch.randperm(max(m, n), generator=gen)[:s]     # distinct rows (tall) or columns
+    idx = torch.arange(s)
+    rows, cols = (lines, idx) if m > n else (idx, lines)
+    dev = torch.device("cuda")
+    rows, cols, cls = rows.to(dev), cols.to(dev), cls.to(dev)
+    grad = torch.zeros((1, m, n), dtype=torch.float32, device=dev)
+    grad[0, rows, cols] = torch.from_numpy(classes).to(dev)[cls]
+    vel = torch.stack([grad, grad])
+    for k in (6, 2):
+        if k == 6:
+            out = gpu_lib.anvil_bank_step(grad, vel, 0.95, 0.85, 1.0)
+        else:
+            out = gpu_lib.anvil_bank_step_maps(grad, vel, 0.95, 0.85, 1.0, list(O.ANVIL_MAPS[:k]))
+        torch.cuda.synchronize()
+        assert torch.equal(vel[0], grad) and torch.equal(vel[1], grad)
+        got = out[0, rows, cols].float()
+        exp = torch.from_numpy(want[k]).to(dev)[cls]
+        assert torch.equal(got, exp), (k, got[:8], exp[:8])
+        assert int(torch.count_nonzero(out)) == s
+        del out
+    del grad, vel
+    gpu_lib.release_workspaces()
+    torch.cuda.empty_cache()

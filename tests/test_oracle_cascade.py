@@ -214,3 +214,36 @@ def test_ns5_table_lands_in_its_band():
     s = np.linspace(0.01, 1.0, 5001)
     f = _F_of(NS5, s)
     assert np.all((f > 0.6) & (f < 1.25))
+
+
+@pytest.mark.parametrize("m,n", [(1032, 1032), (2064, 1040)])
+def test_permuted_diagonal_is_exact_scalar_cascade(m, n):
+    """On a permuted diagonal of powers of two every product of the cascade has at most one
+    nonzero term, so the whole cascade reduces to the scalar maps with the page's rounding steps:
+    the update must be the same permutation of the cascade of a 64x64 diagonal with the same trace
+    (hence the same d), bit for bit, and zero elsewhere.  Pins the operand order of the Gram and
+    the apply (a transposed or swapped operand pairs a value with another line's map: planted in
+    the wide apply, this fails); mistakes that move both runs alike (such as d) are pinned by the
+    closed-form tests above.  Two maps, so that the three classes are still apart (six maps take
+    all of them to 1 within a few bf16 steps)."""
+    from tests.helpers import sigma_classes
+    s = min(m, n)
+    r, counts = sigma_classes(s)
+    classes = np.array([1.0, 0.5, 0.25], np.float32)
+    diag = np.zeros(64, np.float32)
+    diag[:3] = classes
+    diag[3:3 + r] = 16.0
+    maps = O.ANVIL_MAPS[:2]
+    small = O.cascade(np.diag(diag)[None], split=True, maps=maps)[0]
+    want_cls = np.array([small[i, i] for i in range(3)], np.float32)
+    rng = np.random.default_rng(m + n)
+    cls = rng.permutation(np.concatenate([np.full(c, i) for i, c in enumerate(counts)]))
+    lines = rng.permutation(max(m, n))[:s]
+    idx = np.arange(s)
+    rows, cols = (lines, idx) if m > n else (idx, lines)
+    X = np.zeros((1, m, n), np.float32)
+    X[0, rows, cols] = classes[cls]
+    out = O.cascade(X, maps=maps)[0]          # more than 1024 rows: split by the page's rule
+    assert np.array_equal(out[rows, cols], want_cls[cls])
+    assert np.count_nonzero(out) == s
+    assert len(set(want_cls.tolist())) == 3   # the three classes stay distinguishable
