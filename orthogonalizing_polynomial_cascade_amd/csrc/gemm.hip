@@ -427,8 +427,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
   // C[i][j] with i = l%32 and j = 8(r/4) + 4(l/32) + r%4, i.e. runs of 4 consecutive columns of
   // one row, which go to LDS as one 16-byte write.  The rows then leave LDS 8 columns per lane
   // and go to memory as coalesced 16-byte stores; the mirror of a symmetric tile is read down the
-  // LDS columns and also leaves as 16-byte stores.
+  // LDS columns and leaves as 16-byte stores too, four lanes covering 64 contiguous bytes of a
+  // mirrored row (16 rows per store instruction).  Rows 8..15 and 24..31 of the block are stored
+  // with their columns XOR 16, so that the four 8-row groups read by one mirror instruction fall
+  // in two disjoint halves of the banks (two accesses per bank, the minimum for 64 lanes).
   float* epi = reinterpret_cast<float*>(smem) + wave * 32 * C::kEpiPitch;
+  auto ep = [&](int row, int col) {
+    return epi + row * C::kEpiPitch + (col ^ ((row & 8) << 1));
+  };
   uint16_t* Cb = p.C + b * p.strideC;
   const bool diag_tile = (OP != OP_APPLY) && ti == tj;
   float tsum = 0.0f;
@@ -445,7 +451,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
       for (int q = 0; q < 4; ++q) {
         const int row = lane & 31;
         const int col = fn * 32 + 8 * q + 4 * (lane >> 5);
-        *reinterpret_cast<f32x4_t*>(epi + row * C::kEpiPitch + col) =
+        *reinterpret_cast<f32x4_t*>(ep(row, col)) =
             f32x4_t{acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1], acc[fm][fn][4 * q + 2],
                     acc[fm][fn][4 * q + 3]};
       }
@@ -463,8 +469,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
       const int gi = gi0 + row;
       const int gj = gj0 + col;
       if (gi >= p.M || gj >= p.N) continue;
-      const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(epi + row * C::kEpiPitch + col);
-      const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(epi + row * C::kEpiPitch + col + 4);
+      const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(ep(row, col));
+      const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(ep(row, col + 4));
       float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
       u32x4_t out;
       if constexpr (OP == OP_APPLY) {
@@ -497,9 +503,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
             v[2 * e + 1] = ba1 + cq1;
           }
           // the mirror pass below reads the combined value back
-          *reinterpret_cast<f32x4_t*>(epi + row * C::kEpiPitch + col) =
+          *reinterpret_cast<f32x4_t*>(ep(row, col)) =
               f32x4_t{v[0], v[1], v[2], v[3]};
-          *reinterpret_cast<f32x4_t*>(epi + row * C::kEpiPitch + col + 4) =
+          *reinterpret_cast<f32x4_t*>(ep(row, col + 4)) =
               f32x4_t{v[4], v[5], v[6], v[7]};
         }
 #pragma unroll
@@ -528,12 +534,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
     if constexpr (OP != OP_APPLY) {
       wait_lds();
       __builtin_amdgcn_wave_barrier();
-      // mirror: C[gj][gi .. gi+7] from LDS column gj, rows gi .. gi+7 (8-row groups)
+      // mirror: C[gj][gi .. gi+7] from LDS column gj, rows gi .. gi+7 (8-row groups); lanes
+      // 4c .. 4c+3 of a pass take the four groups of one column
 #pragma unroll
       for (int pass = 0; pass < (C::kWTN * 4) / 64; ++pass) {
         const int item = pass * 64 + lane;
-        const int col = item % C::kWTN;
-        const int rq = item / C::kWTN;
+        const int col = item / 4;
+        const int rq = item % 4;
         const int gj = gj0 + col;
         const int gi = gi0 + rq * 8;
         if (gj >= p.N || gi >= p.M) continue;
@@ -542,7 +549,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             if (gi + e < gj) {
-              const float x = epi[(rq * 8 + e) * C::kEpiPitch + col];
+              const float x = *ep(rq * 8 + e, col);
               Cb[(int64_t)gj * p.ldc + gi + e] = (uint16_t)f32_to_bf16(x);
             }
           }
@@ -550,7 +557,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
         }
         float v[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = epi[(rq * 8 + e) * C::kEpiPitch + col];
+        for (int e = 0; e < 8; ++e) v[e] = *ep(rq * 8 + e, col);
         u32x4_t out;
 #pragma unroll
         for (int e = 0; e < 4; ++e) out[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
