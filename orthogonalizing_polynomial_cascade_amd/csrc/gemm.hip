@@ -510,10 +510,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) out[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
-        if (!diag_tile) {
+        if (!diag_tile || gi <= gj) {
           *reinterpret_cast<u32x4_t*>(Cb + (int64_t)gi * p.ldc + gj) = out;
-        } else {
-          // diagonal tile: entries with gi <= gj only (the mirror pass writes the rest)
+        } else if (gi < gj + 8) {
+          // a diagonal tile's piece that straddles the diagonal: entries with gi <= gj + e only
+          // (the mirror pass writes the rest; pieces wholly below the diagonal are all its)
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             if (gi <= gj + e) {
@@ -521,6 +522,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
               Cb[(int64_t)gi * p.ldc + gj + e] = (uint16_t)((e & 1) ? (w >> 16) : (w & 0xFFFFu));
             }
           }
+        }
+        if (diag_tile) {
           if constexpr (OP == OP_GRAM) {
             if (gi >= gj && gi < gj + 8) {
               const uint32_t w = out[(gi - gj) >> 1];
