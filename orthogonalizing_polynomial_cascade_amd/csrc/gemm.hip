@@ -428,12 +428,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
   // one row, which go to LDS as one 16-byte write.  The rows then leave LDS 8 columns per lane
   // and go to memory as coalesced 16-byte stores; the mirror of a symmetric tile is read down the
   // LDS columns and leaves as 16-byte stores too, four lanes covering 64 contiguous bytes of a
-  // mirrored row (16 rows per store instruction).  Rows 8..15 and 24..31 of the block are stored
-  // with their columns XOR 16, so that the four 8-row groups read by one mirror instruction fall
-  // in two disjoint halves of the banks (two accesses per bank, the minimum for 64 lanes).
+  // mirrored row (16 rows per store instruction).  Rows 16..31 of the block are stored with their
+  // columns XOR 16: with the 68-word row pitch, the four 8-row groups read by one mirror
+  // instruction (16 columns each) then cover 64 distinct banks of 64, or every bank of 32 twice.
   float* epi = reinterpret_cast<float*>(smem) + wave * 32 * C::kEpiPitch;
   auto ep = [&](int row, int col) {
-    return epi + row * C::kEpiPitch + (col ^ ((row & 8) << 1));
+    return epi + row * C::kEpiPitch + (col ^ (row & 16));
   };
   uint16_t* Cb = p.C + b * p.strideC;
   const bool diag_tile = (OP != OP_APPLY) && ti == tj;
