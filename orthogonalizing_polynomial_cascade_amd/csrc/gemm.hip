@@ -12,7 +12,8 @@
 //          epilogue bf16(acc); optional trace partials of the bf16 diagonal.
 //   poly   B = b A + c A A   (A symmetric, so A A = A A^T: P = Q = A, K-contiguous)
 //          epilogue bf16(b * A[i][j] + c * acc).
-//   apply  tall: C = a X + X B   (P = X, Q = rows of B; B symmetric so B[k][j] = B[j][k])
+//   apply  tall: C = a X + X B   (P = X; Q(j, k) = B[k][j], K-major: B is symmetric, and its
+//                                 rows k give whole row pieces where B[j][k] gives half lines)
 //          wide: C = a X + B X   (P = B, Q(j, k) = X[k][j]: K-major)
 //          epilogue bf16(a * X[i][j] + acc), or with split rounding
 //          bf16(bf16(acc) + a * X[i][j]) (the page's two-kernel form for banks of > 1024 rows).
@@ -22,16 +23,17 @@
 // are exactly symmetric.  Inside a diagonal tile only entries with i <= j are stored directly.
 //
 // Pipeline (CDNA4 / gfx950):
-//  * Operand slabs (rows x 64 k) travel HBM -> LDS with buffer_load_dwordx4 ... lds (16 bytes per
-//    lane straight into LDS, no register staging) through a ring of STAGES LDS buffers; the loads
-//    for slab k+STAGES-1 are in flight while slab k feeds the MFMAs.  Lanes outside the matrix
-//    (ragged M, N or K edges) get an offset past the buffer's range, which loads zeros.
-//  * K-contiguous slabs are stored [row][64 k] with 16-byte slots XOR-swizzled by row, so that
+//  * Operand slabs (rows x BK k, BK = 64 or 32) travel HBM -> LDS with buffer_load_dwordx4 ... lds
+//    (16 bytes per lane straight into LDS, no register staging) through a ring of STAGES LDS
+//    buffers; the loads for slab k+STAGES-1 are in flight while slab k feeds the MFMAs.  Lanes
+//    outside the matrix (ragged M, N or K edges) get an offset past the buffer's range, which
+//    loads zeros.
+//  * K-contiguous slabs are stored [row][BK k] with 16-byte slots XOR-swizzled by row, so that
 //    an MFMA operand (32 rows x 8 k) is one ds_read_b128 per lane without bank conflicts.
-//  * K-major slabs (X read down its columns) are stored [64 k][rows] as they arrive, slots
-//    swizzled by k; an MFMA operand is two ds_read_b64_tr_b16, the LDS transpose read: within a
-//    16-lane group, lanes 4j..4j+3 point at 16 consecutive rows of k-row j and lane r receives
-//    the 4 k-values of row r.  No VALU transposes.
+//  * K-major slabs (X read down its columns, B by its rows k) are stored [BK k][rows] as they
+//    arrive, slots swizzled by k; an MFMA operand is two ds_read_b64_tr_b16, the LDS transpose
+//    read: within a 16-lane group, lanes 4j..4j+3 point at 16 consecutive rows of k-row j and
+//    lane r receives the 4 k-values of row r.  No VALU transposes.
 //  * Each wave owns a (BM/WM) x (BN/WN) block of 32x32 MFMA fragments.  In the Gram, each group
 //    of 8 slabs (512 k) is accumulated into fresh registers and then added to the running sums
 //    with IEEE fp32 adds (one MFMA accumulation chain over thousands of k drifts from an fp64
@@ -40,8 +42,8 @@
 //  * Tiles are ordered so that consecutive tiles of one matrix land on the same XCD (hardware
 //    dispatches workgroups round-robin over the 8 XCDs, each with its own L2).
 //  * The epilogue goes through LDS, 32 rows at a time per wave: rows leave as 16-byte stores, and
-//    the mirror of a symmetric tile is read down the LDS columns and also leaves as 16-byte
-//    stores.
+//    the mirror of a symmetric tile is read down the LDS columns and leaves as 16-byte stores,
+//    four lanes per mirrored row.
 //
 // Shapes: M, N, K are multiples of 8 (16-byte rows).
 #include <atomic>
