@@ -620,13 +620,15 @@ hipError_t launch(GemmParams p, int64_t g, hipStream_t stream) {
 }
 
 // Tile configurations (measured on MI355X over the five bank shapes):
-//  * Gram and polynomial: 128x128 tiles, 2x2 waves of 64x64, 64-deep slabs, two LDS stages
-//    (64 KB), so two workgroups share a CU.  The Gram accumulates per slab (long K); the
-//    polynomial (K = s) accumulates directly.
-//  * Apply: 128x256 tiles, 2x2 waves of 64x128, 32-deep slabs, three stages (72 KB, two
-//    workgroups per CU) when the stack fills at least one full round of 512 workgroups;
-//    otherwise 128x128 tiles (2x2 waves of 64x64, 64-deep slabs, two stages), which keep more
-//    CUs busy on small stacks.
+//  * Gram: 128x128 tiles, 2x2 waves of 64x64, 64-deep slabs, two LDS stages (64 KB), so two
+//    workgroups share a CU; it sums groups of 8 slabs (long K).
+//  * Polynomial: the same tiles and ring with 2x4 waves of 64x32 (eight waves, four per SIMD over
+//    the two workgroups: more waves to cover each other's waits); accumulates directly (K = s).
+//  * Apply: 128x256 tiles, 2x4 waves of 64x64, 32-deep slabs, two stages (48 KB; two workgroups
+//    per CU, 16 waves) when the stack fills at least half a round of 512 workgroups; otherwise
+//    128x128 tiles (2x4 waves of 64x32, 64-deep slabs, two stages), which keep more CUs busy on
+//    small stacks.  The wave layout and ring depth change no arithmetic: an element's MFMA chain
+//    over k and its epilogue are the same in every configuration.
 constexpr int kSymTile = 128;
 // The Gram (K = the long side, up to thousands) sums each group of 8 slabs (512 k) in fresh
 // registers and adds the group sums to the running sums: on low-rank-dominated inputs one long
@@ -685,7 +687,7 @@ hipError_t launch_poly(const uint16_t* a, uint16_t* bout, float coef_b, float co
   p.beta = coef_c;
   p.tiles_m = p.tiles_n = ceil_div(s, kSymTile);
   p.tiles = p.tiles_m * (p.tiles_m + 1) / 2;
-  return launch<OP_POLY, false, false, 128, 128, 2, 2, 2, 64, 0>(p, g, stream);
+  return launch<OP_POLY, false, false, 128, 128, 2, 4, 2, 64, 0>(p, g, stream);
 }
 
 template <int BM, int BN, int WM, int WN, int STAGES, int BK>
@@ -737,9 +739,9 @@ hipError_t launch_apply_cfg(const uint16_t* x, const uint16_t* bm, uint16_t* c, 
 hipError_t launch_apply(const uint16_t* x, const uint16_t* bm, uint16_t* c, float coef_a,
                         bool split, const Shape& sh, hipStream_t stream) {
   const int64_t wide_tiles = (int64_t)ceil_div(sh.m, 128) * ceil_div(sh.n, 256) * sh.g;
-  if (wide_tiles >= kFullRound)
-    return launch_apply_cfg<128, 256, 2, 2, 3, 32>(x, bm, c, coef_a, split, sh, stream);
-  return launch_apply_cfg<128, 128, 2, 2, 2, 64>(x, bm, c, coef_a, split, sh, stream);
+  if (2 * wide_tiles >= kFullRound)
+    return launch_apply_cfg<128, 256, 2, 4, 2, 32>(x, bm, c, coef_a, split, sh, stream);
+  return launch_apply_cfg<128, 128, 2, 4, 2, 64>(x, bm, c, coef_a, split, sh, stream);
 }
 
 }  // namespace anvil
