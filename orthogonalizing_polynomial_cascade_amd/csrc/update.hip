@@ -65,20 +65,25 @@ __global__ __launch_bounds__(kThreads) void lane_power_rows(const uint16_t* __re
   if (lane == 0) power[b * m + row] = s / static_cast<float>(n);
 }
 
-// Column lanes (rows < cols): a block covers 256 columns (32 chunks of 8) and 8 row groups; each
-// thread sums every 8th row of its chunk, then the row groups are added in order through LDS.
+// Column lanes (rows < cols): a block covers 64 columns (8 chunks of 8) and 32 row groups; each
+// thread sums every 32nd row of its chunk (eight lanes read one row's 128 bytes), then the row
+// groups are added in order through LDS.  Small blocks so that even a few wide matrices give
+// thousands of workgroups.
+constexpr int kColChunks = 8;
+constexpr int kRowGroups = kThreads / kColChunks;
 __global__ __launch_bounds__(kThreads) void lane_power_cols(const uint16_t* __restrict__ u,
                                                             float* __restrict__ power, int m,
                                                             int n) {
-  __shared__ float part[8][257];
-  const int chunk = threadIdx.x & 31;
-  const int rg = threadIdx.x >> 5;
-  const int col0 = blockIdx.x * 256 + chunk * 8;
+  __shared__ float part[kRowGroups][kColChunks * 8 + 1];
+  const int chunk = threadIdx.x % kColChunks;
+  const int rg = threadIdx.x / kColChunks;
+  const int col0 = blockIdx.x * (kColChunks * 8) + chunk * 8;
   const int64_t b = blockIdx.y;
   float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (col0 < n) {
     const uint16_t* base = u + b * (int64_t)m * n + col0;
-    for (int row = rg; row < m; row += 8) {
+#pragma unroll 4
+    for (int row = rg; row < m; row += kRowGroups) {
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(base + (int64_t)row * n);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -94,12 +99,13 @@ __global__ __launch_bounds__(kThreads) void lane_power_cols(const uint16_t* __re
 #pragma unroll
   for (int e = 0; e < 8; ++e) part[rg][chunk * 8 + e] = s[e];
   __syncthreads();
-  const int col = blockIdx.x * 256 + threadIdx.x;
-  if (col < n) {
-    float t = 0.0f;
-#pragma unroll
-    for (int g = 0; g < 8; ++g) t += part[g][threadIdx.x];
-    power[b * n + col] = t / static_cast<float>(m);
+  if (threadIdx.x < kColChunks * 8) {
+    const int col = blockIdx.x * (kColChunks * 8) + threadIdx.x;
+    if (col < n) {
+      float t = 0.0f;
+      for (int g = 0; g < kRowGroups; ++g) t += part[g][threadIdx.x];
+      power[b * n + col] = t / static_cast<float>(m);
+    }
   }
 }
 
@@ -166,12 +172,13 @@ struct DecayArgs {
 };
 
 // Elementwise: u <- bf16(u * scale[lane]) (if scale), write u back (if write_u), then the decay
-// (if d.param).  8 elements per thread per step.
+// (if d.param).  8 elements per thread per step.  Column lanes read their 8 scales with two
+// 16-byte loads when the scale array is 16-byte aligned (vec_scale).
 __global__ __launch_bounds__(kThreads) void scale_decay(uint16_t* __restrict__ u,
                                                         const float* __restrict__ scale,
-                                                        bool write_u, DecayArgs d, int m, int n,
-                                                        bool row_lanes, int64_t chunks_per_matrix,
-                                                        int64_t g) {
+                                                        bool vec_scale, bool write_u, DecayArgs d,
+                                                        int m, int n, bool row_lanes,
+                                                        int64_t chunks_per_matrix, int64_t g) {
   const int64_t total = chunks_per_matrix * g;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total; c += stride) {
@@ -189,11 +196,25 @@ __global__ __launch_bounds__(kThreads) void scale_decay(uint16_t* __restrict__ u
     }
     if (scale != nullptr) {
       const float* sb = scale + b * (row_lanes ? m : n);
+      float sv[8];
+      if (row_lanes) {
+        const float s = sb[row];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float s = row_lanes ? sb[row] : sb[col + e];
-        x[e] = bf16_to_f32(f32_to_bf16(x[e] * s));
+        for (int e = 0; e < 8; ++e) sv[e] = s;
+      } else if (vec_scale) {
+        const f32x4_t s0 = *reinterpret_cast<const f32x4_t*>(sb + col);
+        const f32x4_t s1 = *reinterpret_cast<const f32x4_t*>(sb + col + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sv[e] = s0[e];
+          sv[e + 4] = s1[e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sv[e] = sb[col + e];
       }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = bf16_to_f32(f32_to_bf16(x[e] * sv[e]));
       if (write_u) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) uv[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
@@ -261,7 +282,9 @@ hipError_t launch_equalize(uint16_t* u, float* lane_energy, double beta2, float*
     hipLaunchKernelGGL(lane_power_rows, dim3((unsigned)((sh.m + 3) / 4), (unsigned)sh.g),
                        dim3(kThreads), 0, stream, u, power, sh.m, sh.n);
   } else {
-    hipLaunchKernelGGL(lane_power_cols, dim3((unsigned)((sh.n + 255) / 256), (unsigned)sh.g),
+    hipLaunchKernelGGL(lane_power_cols,
+                       dim3((unsigned)((sh.n + kColChunks * 8 - 1) / (kColChunks * 8)),
+                            (unsigned)sh.g),
                        dim3(kThreads), 0, stream, u, power, sh.m, sh.n);
   }
   hipError_t e = hipGetLastError();
@@ -274,8 +297,10 @@ hipError_t launch_equalize(uint16_t* u, float* lane_energy, double beta2, float*
   if (e != hipSuccess) return e;
   DecayArgs d{param, mantissa, gate, lr, wd, wd_dev};
   const int64_t cpm = (int64_t)sh.m * sh.n / 8;
+  // the scale rows start at multiples of 8 floats from `scale`: 16-byte loads need only its base
+  const bool vec = (reinterpret_cast<uintptr_t>(scale) & 15u) == 0;
   hipLaunchKernelGGL(scale_decay, dim3((unsigned)elementwise_blocks(cpm * sh.g)), dim3(kThreads),
-                     0, stream, u, scale, true, d, sh.m, sh.n, rows, cpm, sh.g);
+                     0, stream, u, scale, vec, true, d, sh.m, sh.n, rows, cpm, sh.g);
   return hipGetLastError();
 }
 
@@ -284,7 +309,7 @@ hipError_t launch_decay(uint16_t* param, uint16_t* mantissa, const uint16_t* u, 
   DecayArgs d{param, mantissa, gate, lr, wd, nullptr};
   const int64_t cpm = (int64_t)sh.m * sh.n / 8;
   hipLaunchKernelGGL(scale_decay, dim3((unsigned)elementwise_blocks(cpm * sh.g)), dim3(kThreads),
-                     0, stream, const_cast<uint16_t*>(u), nullptr, false, d, sh.m, sh.n,
+                     0, stream, const_cast<uint16_t*>(u), nullptr, false, false, d, sh.m, sh.n,
                      sh.m >= sh.n, cpm, sh.g);
   return hipGetLastError();
 }
