@@ -87,7 +87,7 @@ def load(path: str | None = None):
 
 def _check(fn: str, status: int):
     if status != ANVIL_OK:
-        raise AnvilError(fn, status, _lib)
+        raise AnvilError(fn, status, load())
 
 
 def _stream(stream):
@@ -107,6 +107,10 @@ def _need(t, name, dtype, shape=None):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be on the GPU (got {t.device})")
+    if t.device.index is not None and t.device.index != torch.cuda.current_device():
+        # the library launches on the current HIP device and takes plain device pointers
+        raise ValueError(f"{name} is on {t.device}, not on the current device "
+                         f"cuda:{torch.cuda.current_device()} (use torch.cuda.set_device)")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
     if not t.is_contiguous():
