@@ -185,6 +185,27 @@ def test_workspace_covers_the_equalizer_scratch(lib):
         assert lib.anvil_workspace_bytes(g, m, n) >= base + 2 * g * lanes * 4
 
 
+def test_plain_c_consumer(lib, tmp_path):
+    """tests/c_consumer.c, compiled as C11 by the host compiler against include/anvil.h alone and
+    linked to libanvil.so, runs the host-side contract (status strings, workspace sizes, empty
+    stacks, argument checks that reject a call before anything is launched) with no GPU."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    pkg = os.path.dirname(anvil.LIB_PATH)
+    exe = str(tmp_path / "c_consumer")
+    src = os.path.join(root, "tests", "c_consumer.c")
+    r = subprocess.run([cc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-I",
+                        os.path.join(root, "include"), src, "-L", pkg, "-lanvil",
+                        f"-Wl,-rpath,{pkg}", "-o", exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
+
+
 def test_map_table_entry_point_checks(lib):
     table = (ctypes.c_float * 6)(3.0, -4.0, 2.0, 3.0, -4.0, 2.0)
     tp = ctypes.cast(table, ctypes.c_void_p)
