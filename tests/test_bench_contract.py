@@ -32,5 +32,6 @@ def test_flop_and_byte_counts():
     assert f["poly"] == 6 * g * s * s * (s + 1)
     assert f["apply"] == 6 * g * 2 * s * s * L
     assert f["total"] == f["gram"] + f["poly"] + f["apply"]
+    assert f["dense"] == 6 * g * (4 * s * s * L + 2 * s ** 3)   # full Gram and full A*A
     assert bench.flops(g, n, m) == f                  # wide is the transpose of tall
     assert bench.momentum_bytes(g, m, n) == 22 * g * m * n
