@@ -88,3 +88,46 @@ def test_max_size_permuted_diagonal(gpu_lib, m, n):
     del grad, vel
     gpu_lib.release_workspaces()
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("m,n", [(65536, 16384), (16384, 65536)])
+def test_max_size_bank_update_composes_the_stages(gpu_lib, m, n):
+    """The whole bank update on one matrix of 2^30 elements (row lanes for 65536 x 16384, column
+    lanes for the transpose) equals, bit for bit, the step followed by the equalizer and the decay
+    entry points (each checked against the oracle at smaller sizes): every index and grid of the
+    update kernels at the largest supported size."""
+    import torch
+    gen = torch.Generator(device="cuda").manual_seed(m + n)
+    dev = torch.device("cuda")
+    G = torch.randn((1, m, n), generator=gen, device=dev) * 1e-3
+    lanes = gpu_lib.equalizer_lanes(m, n)
+    p0 = (torch.randn((1, m, n), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+    m0 = torch.randint(-32768, 32767, (1, m, n), generator=gen, device=dev,
+                       dtype=torch.int32).to(torch.int16)
+    e0 = torch.rand((1, lanes), generator=gen, device=dev) * 1e-6
+    lr = torch.full((1,), 0.02, device=dev)
+    wd = 0.0125
+    print(f"bank update {m}x{n}", flush=True)
+
+    vel_a = torch.zeros((2, 1, m, n), device=dev)
+    p_a, m_a, e_a = p0.clone(), m0.clone(), e0.clone()
+    u_a = gpu_lib.anvil_bank_update(G, vel_a, 0.95, 0.85, 0.4385, e_a, 0.95, p_a, m_a, wd, lr)
+    torch.cuda.synchronize()
+
+    vel_b = torch.zeros((2, 1, m, n), device=dev)
+    p_b, m_b, e_b = p0.clone(), m0.clone(), e0.clone()
+    u_b = gpu_lib.anvil_bank_step(G, vel_b, 0.95, 0.85, 0.4385)
+    gpu_lib.anvil_equalize(u_b, e_b, 0.95)
+    gpu_lib.anvil_decay_update(p_b, m_b, u_b, wd, lr, vel_b[1])
+    torch.cuda.synchronize()
+
+    assert torch.equal(vel_a, vel_b)
+    assert torch.equal(u_a.view(torch.int16), u_b.view(torch.int16))
+    assert torch.equal(e_a, e_b)
+    assert torch.equal(p_a.view(torch.int16), p_b.view(torch.int16))
+    assert torch.equal(m_a, m_b)
+    assert torch.isfinite(u_a.float()).all()
+    assert not torch.equal(p_a.view(torch.int16), p0.view(torch.int16))   # the decay moved it
+    del G, vel_a, vel_b, p_a, p_b, m_a, m_b, u_a, u_b
+    gpu_lib.release_workspaces()
+    torch.cuda.empty_cache()
