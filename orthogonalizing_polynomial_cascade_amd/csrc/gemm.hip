@@ -46,7 +46,9 @@
 //    four lanes per mirrored row.
 //
 // Shapes: M, N, K are multiples of 8 (16-byte rows).
+#include <algorithm>
 #include <atomic>
+#include <cstdint>
 
 #include "device_common.h"
 #include "launchers.h"
@@ -614,9 +616,24 @@ hipError_t launch(GemmParams p, int64_t g, hipStream_t stream) {
     if (e != hipSuccess) return e;
     configured.fetch_or(bit, std::memory_order_release);
   }
-  p.total = (int)(p.tiles * g);
-  hipLaunchKernelGGL(kern, dim3((unsigned)p.total), dim3(C::kThreads), C::kLdsBytes, stream, p);
-  return hipGetLastError();
+  // A dispatch counts its work-items in 32 bits: a stack whose tiles need more goes out as
+  // consecutive sub-stacks (every matrix keeps its own tiles, so nothing in its arithmetic moves).
+  const int64_t per_launch =
+      std::max<int64_t>(1, int64_t(UINT32_MAX) / ((int64_t)p.tiles * C::kThreads));
+  for (int64_t b0 = 0; b0 < g; b0 += per_launch) {
+    const int64_t gb = std::min(per_launch, g - b0);
+    GemmParams q = p;
+    q.P += b0 * p.strideP;
+    q.Q += b0 * p.strideQ;
+    q.C += b0 * p.strideC;
+    if (q.E) q.E += b0 * p.strideE;
+    if (q.trace) q.trace += b0 * p.trace_slots;
+    q.total = (int)(p.tiles * gb);
+    hipLaunchKernelGGL(kern, dim3((unsigned)q.total), dim3(C::kThreads), C::kLdsBytes, stream, q);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // Tile configurations (measured on MI355X over the five bank shapes):

@@ -18,6 +18,8 @@
 // Three kernels: lane powers (deterministic fixed-order reductions), one workgroup per matrix for
 // the scales and the energy EMA, and one fused elementwise pass that rescales the update, writes
 // it back and applies the decay (HBM-bound: 16 bytes per element with the decay).
+#include <algorithm>
+
 #include "device_common.h"
 #include "launchers.h"
 
@@ -37,32 +39,36 @@ __device__ __forceinline__ float rsqrt_rn(float x) {
   return static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(x)));
 }
 
-// Row lanes (rows >= cols): one wave per row, 8 elements per lane per step, butterfly sum.
+// Row lanes (rows >= cols): one wave per row, 8 elements per lane per step, butterfly sum.  The
+// grid's x extent is capped (a dispatch counts its work-items in 32 bits); waves then take every
+// (gridDim.x * 4)-th row, each row still summed by one wave in the same order.
+constexpr int kMaxRowBlocks = 1 << 20;
 __global__ __launch_bounds__(kThreads) void lane_power_rows(const uint16_t* __restrict__ u,
                                                             float* __restrict__ power, int m,
                                                             int n) {
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * (kThreads / 64) + wave;
   const int64_t b = blockIdx.y;
-  if (row >= m) return;
-  const uint16_t* r = u + (b * m + row) * (int64_t)n;
-  float s = 0.0f;
-  for (int c = lane * 8; c < n; c += 64 * 8) {
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(r + c);
+  const int row_step = gridDim.x * (kThreads / 64);
+  for (int row = blockIdx.x * (kThreads / 64) + wave; row < m; row += row_step) {
+    const uint16_t* r = u + (b * m + row) * (int64_t)n;
+    float s = 0.0f;
+    for (int c = lane * 8; c < n; c += 64 * 8) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(r + c);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float lo = bf16_to_f32(v[e] & 0xFFFFu);
-      const float hi = bf16_to_f32(v[e] >> 16);
-      const float slo = lo * lo;
-      const float shi = hi * hi;
-      s += slo;
-      s += shi;
+      for (int e = 0; e < 4; ++e) {
+        const float lo = bf16_to_f32(v[e] & 0xFFFFu);
+        const float hi = bf16_to_f32(v[e] >> 16);
+        const float slo = lo * lo;
+        const float shi = hi * hi;
+        s += slo;
+        s += shi;
+      }
     }
-  }
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
-  if (lane == 0) power[b * m + row] = s / static_cast<float>(n);
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+    if (lane == 0) power[b * m + row] = s / static_cast<float>(n);
+  }
 }
 
 // Column lanes (rows < cols): a block covers 64 columns (8 chunks of 8) and 32 row groups; each
@@ -279,7 +285,8 @@ hipError_t launch_equalize(uint16_t* u, float* lane_energy, double beta2, float*
   float* power = scratch;
   float* scale = scratch + sh.g * lanes;
   if (rows) {
-    hipLaunchKernelGGL(lane_power_rows, dim3((unsigned)((sh.m + 3) / 4), (unsigned)sh.g),
+    const int row_blocks = std::min((sh.m + 3) / 4, kMaxRowBlocks);
+    hipLaunchKernelGGL(lane_power_rows, dim3((unsigned)row_blocks, (unsigned)sh.g),
                        dim3(kThreads), 0, stream, u, power, sh.m, sh.n);
   } else {
     hipLaunchKernelGGL(lane_power_cols,

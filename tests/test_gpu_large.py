@@ -8,7 +8,7 @@ import pytest
 
 from oracle import anvil_oracle as O
 from orthogonalizing_polynomial_cascade_amd import workloads as W
-from tests.helpers import from_gpu, sigma_classes, to_gpu_f32
+from tests.helpers import assert_gemm_close, from_gpu, sigma_classes, to_gpu_f32
 
 pytestmark = pytest.mark.gpu
 
@@ -131,3 +131,49 @@ def test_max_size_bank_update_composes_the_stages(gpu_lib, m, n):
     del G, vel_a, vel_b, p_a, p_b, m_a, m_b, u_a, u_b
     gpu_lib.release_workspaces()
     torch.cuda.empty_cache()
+
+
+def test_apply_stack_beyond_one_dispatch(gpu_lib):
+    """Eight tall 2^27 x 8 matrices (2^33 elements): their apply has 2^23 tiles of 512 work-items,
+    more than one dispatch counts (32 bits), so it goes out as two launches (7 + 1 matrices).
+    Each matrix of the stack must equal, bit for bit, the apply of that matrix alone (one launch),
+    and sampled rows must match the oracle's apply (split rounding: more than 1024 rows)."""
+    import torch
+    g, m, n = 8, 1 << 27, 8
+    dev = torch.device("cuda")
+    gen = torch.Generator(device="cuda").manual_seed(29)
+    print(f"apply stack {g}x{m}x{n}", flush=True)
+    X = torch.empty((g, m, n), dtype=torch.bfloat16, device=dev)
+    for i in range(g):
+        X[i] = (torch.randn((m, n), generator=gen, device=dev) * 0.1).to(torch.bfloat16)
+    S = torch.randn((g, n, n), generator=gen, device=dev) * 0.3
+    B = (S + S.transpose(1, 2)).to(torch.bfloat16).contiguous()
+    a = O.ANVIL_MAPS[2][0]
+    C = gpu_lib.anvil_apply(X, B, a, True)
+    torch.cuda.synchronize()
+    rows = torch.randint(0, m, (4096,), generator=gen, device=dev)
+    rows[:2] = torch.tensor([0, m - 1], device=dev)
+    Bh = from_gpu(B)
+    for i in (0, 6, 7):
+        Ci = gpu_lib.anvil_apply(X[i:i + 1], B[i:i + 1], a, True)
+        torch.cuda.synchronize()
+        assert torch.equal(C[i].view(torch.int16), Ci[0].view(torch.int16)), i
+        del Ci
+        want = O.apply(from_gpu(X[i, rows])[None], Bh[i:i + 1], a, True, True)
+        assert_gemm_close(from_gpu(C[i, rows])[None], want, f"apply rows of matrix {i}")
+    del X, C, B
+    torch.cuda.empty_cache()
+
+
+def test_row_lanes_beyond_the_grid_cap(gpu_lib):
+    """Row lanes of a 4195336 x 8 update: more rows than the row-lane kernel's capped grid holds
+    waves (2^22), so waves take a second row.  Powers, energies, scales and the rescaled update
+    against the oracle's equalizer, with the bars of the equalizer parity tests."""
+    from tests.test_gpu_update import _check_equalizer, _gpu_equalize
+    g, m, n = 1, (1 << 22) + 1032, 8
+    rng = np.random.default_rng(31)
+    v = rng.standard_normal((g, m, n)) * np.exp(rng.standard_normal((g, m, 1)))
+    u = O.R((v / np.sqrt(m)).astype(np.float32))
+    power = (u.astype(np.float64) ** 2).mean(axis=-1, keepdims=True)
+    energy = (power * np.exp(rng.standard_normal(power.shape))).astype(np.float32)
+    _check_equalizer(u, energy, 0.95, *_gpu_equalize(gpu_lib, u, energy, 0.95))
