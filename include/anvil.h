@@ -32,7 +32,8 @@
  *     anvil_bank_step (released by anvil_release_workspaces).
  *   - No exception crosses the ABI.  NaN and Inf in the data propagate; nothing checks them.
  *   - Thread safety: calls are safe from several threads; the cached workspace is per
- *     (device, stream), so calls on different streams do not share scratch memory.
+ *     (device, stream), so calls on different streams do not share scratch memory, and calls that
+ *     use the cache hold its lock while they enqueue (their enqueues take turns).
  */
 #ifndef ANVIL_H_
 #define ANVIL_H_

@@ -219,12 +219,15 @@ int run_update(const MomentumIn& mi, float* velocity, uint16_t* update, const Up
 std::mutex g_ws_mutex;
 std::map<std::pair<int, hipStream_t>, std::pair<void*, size_t>> g_ws;
 
-// The cached workspace of at least `need` bytes for the current device and `stream`.
-int cached_workspace(size_t need, hipStream_t hs, char** out) {
+// The cached workspace of at least `need` bytes for the current device and `stream`.  `lock`
+// keeps the cache locked until the caller has enqueued its work with the buffer: a call on the
+// same stream from another thread that has to grow it waits until then, and its stream
+// synchronisation before the free then covers that work.
+int cached_workspace(size_t need, hipStream_t hs, char** out, std::unique_lock<std::mutex>* lock) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_status(e);
-  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  *lock = std::unique_lock<std::mutex>(g_ws_mutex);
   auto& slot = g_ws[{dev, hs}];
   if (slot.second < need) {
     if (slot.first) {
@@ -260,14 +263,14 @@ int check_workspace(const void* workspace, size_t workspace_bytes, const Shape& 
 
 // The workspace to use: the caller's (checked against `bufs`) or, when null, the cached one.
 int pick_workspace(void* workspace, size_t workspace_bytes, const Shape& sh, hipStream_t hs,
-                   std::initializer_list<Buf> bufs, char** ws) {
+                   std::initializer_list<Buf> bufs, char** ws, std::unique_lock<std::mutex>* lock) {
   if (workspace) {
     const int st = check_workspace(workspace, workspace_bytes, sh, bufs);
     if (st != ANVIL_OK) return st;
     *ws = static_cast<char*>(workspace);
     return ANVIL_OK;
   }
-  return cached_workspace(layout_for(sh).total, hs, ws);
+  return cached_workspace(layout_for(sh).total, hs, ws, lock);
 }
 
 MomentumIn by_value(const float* grad, float momentum, float fast_beta, float fast_weight) {
@@ -318,9 +321,10 @@ int anvil_bank_step_ws(const float* grad, float* velocity, float momentum, float
   if (!workspace) return ANVIL_ERR_INVALID_ARG;
   const size_t cnt = static_cast<size_t>(sh.g) * sh.m * sh.n;
   char* ws = nullptr;
+  std::unique_lock<std::mutex> lock;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   st = pick_workspace(workspace, workspace_bytes, sh, hs,
-                      {{grad, cnt * 4}, {velocity, cnt * 8}, {out, cnt * 2}}, &ws);
+                      {{grad, cnt * 4}, {velocity, cnt * 8}, {out, cnt * 2}}, &ws, &lock);
   if (st != ANVIL_OK) return st;
   return run_step(by_value(grad, momentum, fast_beta, fast_weight), velocity, out, sh, ws, hs);
 }
@@ -336,7 +340,8 @@ int anvil_bank_step(const float* grad, float* velocity, float momentum, float fa
   if (st != ANVIL_OK) return st;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   char* ws = nullptr;
-  st = cached_workspace(layout_for(sh).total, hs, &ws);
+  std::unique_lock<std::mutex> lock;
+  st = cached_workspace(layout_for(sh).total, hs, &ws, &lock);
   if (st != ANVIL_OK) return st;
   return run_step(by_value(grad, momentum, fast_beta, fast_weight), velocity, out, sh, ws, hs);
 }
@@ -356,8 +361,9 @@ int anvil_bank_step_maps(const float* grad, float* velocity, float momentum, flo
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const size_t cnt = static_cast<size_t>(sh.g) * sh.m * sh.n;
   char* ws = nullptr;
+  std::unique_lock<std::mutex> lock;
   st = pick_workspace(workspace, workspace_bytes, sh, hs,
-                      {{grad, cnt * 4}, {velocity, cnt * 8}, {out, cnt * 2}}, &ws);
+                      {{grad, cnt * 4}, {velocity, cnt * 8}, {out, cnt * 2}}, &ws, &lock);
   if (st != ANVIL_OK) return st;
   float table[kMaxMaps][3];
   for (int k = 0; k < steps; ++k)
@@ -384,8 +390,10 @@ int anvil_bank_step_dev(const void* grad, int grad_dtype, float* velocity, const
   if (st != ANVIL_OK) return st;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   char* ws = nullptr;
+  std::unique_lock<std::mutex> lock;
   st = pick_workspace(workspace, workspace_bytes, sh, hs,
-                      {{grad, cnt * gb}, {velocity, cnt * 8}, {out, cnt * 2}, {scalars, 12}}, &ws);
+                      {{grad, cnt * gb}, {velocity, cnt * 8}, {out, cnt * 2}, {scalars, 12}}, &ws,
+                      &lock);
   if (st != ANVIL_OK) return st;
   const MomentumIn mi{grad, grad_dtype == ANVIL_GRAD_BF16, scalars, 0.0f, 0.0f, 0.0f};
   return run_step(mi, velocity, out, sh, ws, hs);
@@ -418,11 +426,12 @@ int anvil_bank_update_ws(const float* grad, float* velocity, float momentum, flo
   const size_t lb = static_cast<size_t>(sh.g) * anvil::equalizer_lanes(sh) * 4;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   char* ws = nullptr;
+  std::unique_lock<std::mutex> lock;
   st = pick_workspace(workspace, workspace_bytes, sh, hs,
                       {{grad, cnt * 4}, {velocity, cnt * 8}, {update, cnt * 2}, {param, cnt * 2},
                        {mantissa, cnt * 2}, {lane_energy, lb},
                        {eff_lr, static_cast<size_t>(sh.g) * 4}},
-                      &ws);
+                      &ws, &lock);
   if (st != ANVIL_OK) return st;
   const UpdateIn ui{lane_energy, beta2, param, mantissa, eff_wd, nullptr, eff_lr};
   return run_update(by_value(grad, momentum, fast_beta, fast_weight), velocity, update, ui, sh, ws,
@@ -450,11 +459,12 @@ int anvil_bank_update_dev(const void* grad, int grad_dtype, float* velocity,
   const size_t lb = static_cast<size_t>(sh.g) * anvil::equalizer_lanes(sh) * 4;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   char* ws = nullptr;
+  std::unique_lock<std::mutex> lock;
   st = pick_workspace(workspace, workspace_bytes, sh, hs,
                       {{grad, cnt * gb}, {velocity, cnt * 8}, {update, cnt * 2}, {param, cnt * 2},
                        {mantissa, cnt * 2}, {lane_energy, lb},
                        {eff_lr, static_cast<size_t>(sh.g) * 4}, {scalars, 16}},
-                      &ws);
+                      &ws, &lock);
   if (st != ANVIL_OK) return st;
   const MomentumIn mi{grad, grad_dtype == ANVIL_GRAD_BF16, scalars, 0.0f, 0.0f, 0.0f};
   const UpdateIn ui{lane_energy, beta2, param, mantissa, 0.0f, scalars + 3, eff_lr};

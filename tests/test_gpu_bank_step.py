@@ -183,6 +183,48 @@ def test_workspace_regrow_between_shapes(gpu_lib):
     gpu_lib.release_workspaces()
 
 
+def test_threads_on_one_stream_match_sequential(gpu_lib):
+    """Two threads call the cached-workspace entry point on the same stream with shapes of
+    different workspace sizes, one of them releasing the cache after each call, so the cache is
+    freed and grown again while the other thread may be enqueueing: every result must equal the
+    sequential one bit for bit."""
+    import threading
+    import torch
+    shapes = [(2, 200, 328), (3, 1096, 136)]
+    inputs = [to_gpu_f32(_gauss_steps(g, m, n, 17 + k, 1)[0]) for k, (g, m, n) in enumerate(shapes)]
+
+    def step(G):
+        v = torch.zeros((2,) + tuple(G.shape), dtype=torch.float32, device="cuda")
+        return gpu_lib.anvil_bank_step(G, v, 0.95, 0.85, 1.0)
+
+    refs = [step(G) for G in inputs]
+    torch.cuda.synchronize()
+    results = {0: [], 1: []}
+    errors = []
+
+    def run(k):
+        try:
+            for _ in range(8):
+                results[k].append(step(inputs[k]))
+                if k == 0:
+                    gpu_lib.release_workspaces()
+        except Exception as e:      # reported below, on the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=run, args=(k,)) for k in (0, 1)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for k in (0, 1):
+        assert len(results[k]) == 8
+        for r in results[k]:
+            assert torch.equal(r.view(torch.int16), refs[k].view(torch.int16))
+    gpu_lib.release_workspaces()
+
+
 def test_zero_gradient_and_nan(gpu_lib):
     import torch
     g, m, n = 3, 72, 40
