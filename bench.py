@@ -284,9 +284,12 @@ def cpu_baseline(w, budget_s=15.0):
                       f"bf16 rounding emulation), {el:.1f} s"}
 
 
-def run_workload(anvil, name, steps, warmup, with_stages=True):
+def run_workload(anvil, name, steps, warmup, with_stages=True, share=1):
     from orthogonalizing_polynomial_cascade_amd import workloads
     w = workloads.ALL[name]()
+    if share > 1:
+        # one GPU's part of the bank when whole matrices are spread over `share` GPUs
+        w = workloads.scaled(w, g=-(-w.g // share))
     ms, wall, _ = time_bank_step(anvil, w, steps, warmup)
     f = flops(w.g, w.m, w.n)
     rec = {
@@ -320,6 +323,9 @@ def main():
     ap.add_argument("--workload", default="mlp")
     ap.add_argument("--all", action="store_true", help="also report every workload (stderr)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--share", type=int, default=1, metavar="K",
+                    help="time one GPU's share of the bank split by whole matrices over K GPUs "
+                         "(ceil(g/K) matrices) instead of the whole bank")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes three times (the reference "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes) and exit")
@@ -327,6 +333,9 @@ def main():
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the ANVIL bank step runs on a single GPU and has no "
               "cross-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if args.share < 1:
+        print("--share must be at least 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -345,13 +354,18 @@ def main():
         return
     anvil.load()
 
-    w, rec = run_workload(anvil, args.workload, args.steps, args.warmup)
+    w, rec = run_workload(anvil, args.workload, args.steps, args.warmup, share=args.share)
     f = flops(w.g, w.m, w.n)
     apply_us = rec["stage_us"]["apply"]
     apply_flops = f["apply"] / 6
     achieved = apply_flops / (apply_us * 1e-6) / 1e12
+    metric = METRIC
+    if w.name != "mlp" or args.share != 1:
+        metric = (f"ANVIL bank-step matrices/s + TFLOP/s (% bf16 MFMA peak), "
+                  f"{w.g}\u00d7{w.m}\u00d7{w.n} {w.name} bank"
+                  + ("" if args.share == 1 else f" (1/{args.share} share)"))
     line = {
-        "metric": METRIC,
+        "metric": metric,
         "value": rec["matrices_per_s"],
         "unit": "matrices/s",
         "n_gpus": 1,
@@ -365,7 +379,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name} bank {w.g}x{w.m}x{w.n} (fp32 grads, fp32 rails, "
                                f"bf16 cascade, 6 maps)", "g": w.g, "m": w.m, "n": w.n,
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU" if args.share == 1 else
+                   f"one GPU's share of the bank split by whole matrices over {args.share} GPUs"},
         "tflops": rec["tflops"],
         "pct_bf16_peak": rec["pct_bf16_peak"],
         "stage_us": rec["stage_us"],

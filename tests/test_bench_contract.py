@@ -22,6 +22,14 @@ def test_more_than_one_gpu_is_refused(argv, env):
     assert r.stdout == ""
 
 
+def test_share_must_be_positive():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--share", "0"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "--share" in r.stderr
+    assert r.stdout == ""
+
+
 def test_flop_and_byte_counts():
     sys.path.insert(0, ROOT)
     import bench
