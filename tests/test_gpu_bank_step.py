@@ -85,6 +85,28 @@ def test_bank_step_parity(gpu_lib, name, g, m, n):
         assert checked == g, "clearly rectangular Gaussian stacks are well conditioned"
 
 
+@pytest.mark.parametrize("g,m,n,r", [(2, 1096, 136, 1), (2, 200, 328, 2), (1, 264, 264, 3)])
+def test_low_rank_gradient(gpu_lib, g, m, n, r):
+    """Rank-r gradients: after the bf16 cast only rounding noise lies outside the rank-r part; the
+    maps amplify it (to about 0.3-0.45 here, in the oracle too) but not to 1, while the r signal
+    directions come out at singular value 1 (within 0.01) along the input's own singular
+    vectors.  Parity to the oracle as for every step (the noise-floor bar applies: the amplified
+    noise depends on the accumulation order)."""
+    rng = np.random.default_rng(100 + r)
+    G = np.stack([rng.standard_normal((m, r)) @ rng.standard_normal((r, n))
+                  for _ in range(g)]).astype(np.float32)
+    out, y = _run_both(gpu_lib, [G], [(0.95, 0.85, 1.0)], g, m, n, return_lookahead=True)
+    for i in range(g):
+        X = O.R(y[i]).astype(np.float64)
+        Ux, _, Vxt = np.linalg.svd(X, full_matrices=False)
+        Uo, so, Vot = np.linalg.svd(out[i].astype(np.float64), full_matrices=False)
+        assert np.all(np.abs(so[:r] - 1) <= 1e-2), so[:r + 1]
+        assert so[r] <= 0.8, so[:r + 1]
+        # cosines of the principal angles between the input's and the output's signal subspaces
+        assert np.linalg.svd(Ux[:, :r].T @ Uo[:, :r], compute_uv=False).min() >= 0.999
+        assert np.linalg.svd(Vxt[:r] @ Vot[:r].T, compute_uv=False).min() >= 0.999
+
+
 def _well_conditioned(y):
     """Every singular value of the normalised input inside the maps' convergence window
     (sigma/d in [0.002, 1/1.05]), where the six maps land within 0.3 of 1."""
