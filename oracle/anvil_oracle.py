@@ -17,8 +17,10 @@ What it computes (source: modded-nanogpt, `track_1_short/optim/anvil.py`, functi
      Gram recomputed from the current X for every map after the first.
 
 Precision model (the plainest reading of the page where it leaves the precision open):
-  * elementwise steps are fp32 operations, each rounded separately (numpy float32 arithmetic,
-    no fused multiply-add);
+  * elementwise steps are fp32 operations, each rounded separately (numpy float32 arithmetic),
+    except the lerps: the page calls torch's `lerp_`, whose definition in the library takes the
+    difference of the end points and then one fused multiply-add about the nearer end point
+    (`lerp` below, pinned bit for bit against torch.lerp on the CPU);
   * every matrix product is taken in fp64 from the bf16 operands, rounded once to fp32 (the
     accumulator type of a bf16 GEMM), and only then rounded to bf16 where the page stores bf16;
   * the polynomial epilogue b*A + c*(A@A) and the apply epilogue a*X + P are fp32 before their one
@@ -116,9 +118,59 @@ def rail_scalars(step: int):
     return 0.95, RAIL_FAST_BETA, fast_weight
 
 
+def fma32(a, b, c):
+    """fp32 fused multiply-add: a*b + c rounded once to fp32 (round to nearest, ties to even).
+
+    The product of two fp32 values is exact in fp64.  The fp64 sum s = a*b + c and its exact error
+    e (Knuth's two-sum, a*b + c == s + e) then decide the one fp32 rounding: rounding s is already
+    the correctly rounded result unless s lies exactly halfway between two fp32 values, and then
+    the sign of e says on which side of that midpoint the exact sum lies (e == 0: ties to even,
+    which is what the cast of s does).  A midpoint in fp32's normal range has the fp64 pattern
+    1 followed by 28 zeros below the fp32 mantissa; those entries and the ones in fp32's
+    subnormal range take the careful path.
+    """
+    a = np.asarray(a, dtype=F32).astype(np.float64)
+    b = np.asarray(b, dtype=F32).astype(np.float64)
+    c = np.asarray(c, dtype=F32).astype(np.float64)
+    a, b, c = np.broadcast_arrays(a, b, c)
+    with np.errstate(over="ignore", invalid="ignore"):
+        p = a * b
+        s = p + c
+        r = s.astype(F32)
+        low = np.ascontiguousarray(s).view(np.uint64) & np.uint64(0x1FFFFFFF)
+        careful = (low == np.uint64(0x10000000)) | (np.abs(s) < 2.0 ** -126)
+        if not careful.any():
+            return r
+        idx = np.nonzero(careful)
+        pi, ci, si = p[idx], c[idx], s[idx]
+        bv = si - pi
+        e = (pi - (si - bv)) + (ci - bv)
+        ri = r[idx]
+        r64 = ri.astype(np.float64)
+        other = np.where(si > r64, np.nextafter(ri, F32(np.inf)), np.nextafter(ri, F32(-np.inf)))
+        o64 = other.astype(np.float64)
+        at_midpoint = np.isfinite(o64) & (si == (r64 + o64) / 2) & (e != 0)
+        beyond = np.sign(e) == np.sign(o64 - r64)
+        r = np.array(r, copy=True)
+        r[idx] = np.where(at_midpoint & beyond, other, ri)
+        return r
+
+
 def lerp(start, end, weight):
-    """The documented lerp, start + weight * (end - start), one fp32 rounding per operation."""
-    return start + weight * (end - start)
+    """torch's lerp, which the page calls (`lerp_`) for both rails and the Nesterov lookahead.
+
+    The library forms it about the nearer end: for |weight| < 1/2 it is start + weight*(end - start),
+    otherwise end + (weight - 1)*(end - start); the difference end - start is one fp32 operation and
+    the multiply-add that follows is fused (one rounding).  weight - 1 is an fp32 subtraction
+    (exact for weights in [1/2, 1]).  The weight is one scalar for the whole call.
+    """
+    start = np.asarray(start, dtype=F32)
+    end = np.asarray(end, dtype=F32)
+    w = F32(weight)
+    diff = (end - start).astype(F32)
+    if abs(w) < F32(0.5):
+        return fma32(w, diff, start)
+    return fma32(w - F32(1.0), diff, end)
 
 
 def momentum_step(grad, velocity, momentum, fast_beta, fast_weight):

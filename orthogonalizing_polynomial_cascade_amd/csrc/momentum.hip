@@ -1,12 +1,14 @@
 // Kernel 1: fused twin-rail momentum and bf16 cast.
 //
-// Source: modded-nanogpt anvil.py, `anvil_cascade`, momentum block.  Per element, in fp32 with
-// every operation rounded on its own (this file is built with -ffp-contract=off):
-//   v0 <- v0 + wf * (g - v0)            wf = 1.0f - fast_beta
-//   v1 <- v1 + ws * (g - v1)            ws = (float)(1 - 0.98)
-//   blend = w * v0 + (1 - w) * v1       w = fast_weight
-//   y = g + mu * (blend - g)            mu = momentum
+// Source: modded-nanogpt anvil.py, `anvil_cascade`, momentum block.  Per element, in fp32:
+//   v0 <- lerp(v0, g, wf)               wf = 1.0f - fast_beta
+//   v1 <- lerp(v1, g, ws)               ws = (float)(1 - 0.98)
+//   blend = w * v0 + (1 - w) * v1       w = fast_weight; three separately rounded operations
+//   y = lerp(g, blend, mu)              mu = momentum
 //   x = bf16(y)                         round to nearest even
+// where lerp is torch's (the page calls `lerp_`): d = end - start, then one fused multiply-add
+// about the nearer end, fma(w, d, start) for |w| < 1/2, else fma(w - 1, d, end).  The file is
+// built with -ffp-contract=off, so the fused operations are exactly the explicit fmaf calls.
 //
 // HBM-bound: each element reads grad (4 B, or 2 B for a bf16 gradient, which the page widens to
 // fp32 exactly before the lerps) and both rails (8 B) and writes both rails (8 B) and x (2 B) —
@@ -22,13 +24,27 @@ namespace anvil {
 
 namespace {
 
-struct RailWeights {
-  float wf, ws, w, omw, mu;
+// One lerp weight as torch forms it: the multiplier of end - start and which end point the fused
+// multiply-add starts from (the nearer one).
+struct LerpWeight {
+  float coef;
+  bool from_end;
 };
 
-__device__ __forceinline__ float lerp_doc(float start, float end, float weight) {
-  return start + weight * (end - start);
+__host__ __device__ __forceinline__ LerpWeight lerp_weight(float w) {
+  const bool big = !(w > -0.5f && w < 0.5f);
+  return LerpWeight{big ? w - 1.0f : w, big};
 }
+
+__device__ __forceinline__ float lerp_torch(float start, float end, LerpWeight lw) {
+  const float d = end - start;
+  return __builtin_fmaf(lw.coef, d, lw.from_end ? end : start);
+}
+
+struct RailWeights {
+  LerpWeight wf, ws, mu;
+  float w, omw;
+};
 
 // The rail weights from the fp32 scalars (momentum, fast_beta, fast_weight): 1 - fast_beta and
 // 1 - fast_weight are fp32 subtractions; the slow weight is the host double 1 - 0.98 taken as
@@ -36,11 +52,11 @@ __device__ __forceinline__ float lerp_doc(float start, float end, float weight) 
 __host__ __device__ __forceinline__ RailWeights rail_weights(float momentum, float fast_beta,
                                                              float fast_weight) {
   RailWeights rw;
-  rw.wf = 1.0f - fast_beta;
-  rw.ws = static_cast<float>(1.0 - 0.98);
+  rw.wf = lerp_weight(1.0f - fast_beta);
+  rw.ws = lerp_weight(static_cast<float>(1.0 - 0.98));
   rw.w = fast_weight;
   rw.omw = 1.0f - fast_weight;
-  rw.mu = momentum;
+  rw.mu = lerp_weight(momentum);
   return rw;
 }
 
@@ -92,10 +108,10 @@ __global__ __launch_bounds__(256) void momentum_kernel(const GradT* __restrict__
       float y[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        a[u][e] = lerp_doc(a[u][e], g[u][e], rw.wf);
-        c[u][e] = lerp_doc(c[u][e], g[u][e], rw.ws);
+        a[u][e] = lerp_torch(a[u][e], g[u][e], rw.wf);
+        c[u][e] = lerp_torch(c[u][e], g[u][e], rw.ws);
         const float blend = rw.w * a[u][e] + rw.omw * c[u][e];
-        y[e] = lerp_doc(g[u][e], blend, rw.mu);
+        y[e] = lerp_torch(g[u][e], blend, rw.mu);
       }
       // the rails are next read one step later: stream them past the caches
       __builtin_nontemporal_store(a[u], v0 + i);

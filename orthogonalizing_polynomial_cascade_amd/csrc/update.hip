@@ -8,12 +8,15 @@
 // column (reducing over the rows) -- the page's code, whose docstring calls the reduced axis the
 // longer one.  Per matrix, in fp32:
 //   power[l] = mean over the lane of u^2             pre  = sqrt(sum_l power[l] * len)
-//   e[l]    += (1 - beta2) * (power[l] - e[l])        gain = 1 / sqrt(max(e[l], 1e-10))
+//   e[l]     = lerp(e[l], power[l], 1 - beta2)        gain = 1 / sqrt(max(e[l], 1e-10))
 //   post     = sqrt(sum_l (power[l] * len) * gain^2)  scale[l] = bf16(gain * (pre / max(post, 1e-10)))
 //   u       <- bf16(u * scale[lane])
 // then, per element, with the fp32 master m = (param bits << 16) | mantissa:
 //   m <- (m - ((m * [gate * m >= 0]) * wd) * lr[matrix]) - u * lr[matrix]
 //   param bits = high half of m (truncation), mantissa = low half.
+//
+// lerp is torch's, which the page calls (`lerp_`): d = end - start, then one fused multiply-add
+// about the nearer end point, fma(w, d, start) for |w| < 1/2, else fma(w - 1, d, end).
 //
 // Three kernels: lane powers (deterministic fixed-order reductions), one workgroup per matrix for
 // the scales and the energy EMA, and one fused elementwise pass that rescales the update, writes
@@ -137,7 +140,8 @@ __device__ float block_sum(float v, float* red) {
 __global__ __launch_bounds__(kScaleThreads) void lane_scales(const float* __restrict__ power,
                                                              float* __restrict__ energy,
                                                              float* __restrict__ scale, int lanes,
-                                                             int len, float w_ema) {
+                                                             int len, float w_coef,
+                                                             bool w_from_end) {
   __shared__ float red[kScaleThreads / 64];
   const int64_t b = blockIdx.x;
   const float* pw = power + b * lanes;
@@ -153,7 +157,8 @@ __global__ __launch_bounds__(kScaleThreads) void lane_scales(const float* __rest
   float qs = 0.0f;
   for (int l = threadIdx.x; l < lanes; l += kScaleThreads) {
     const float p = pw[l];
-    const float e = en[l] + w_ema * (p - en[l]);
+    const float e0 = en[l];
+    const float e = __builtin_fmaf(w_coef, p - e0, w_from_end ? p : e0);
     en[l] = e;
     const float gain = rsqrt_rn(fmaxf(e, 1e-10f));
     const float pl = p * flen;
@@ -296,10 +301,13 @@ hipError_t launch_equalize(uint16_t* u, float* lane_energy, double beta2, float*
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // 1 - beta2 formed in double and taken as fp32, as the page's lerp weight
+  // 1 - beta2 formed in double and taken as fp32, as the page's lerp weight; the lerp starts
+  // from the nearer end point
   const float w_ema = static_cast<float>(1.0 - beta2);
+  const bool w_from_end = !(w_ema > -0.5f && w_ema < 0.5f);
   hipLaunchKernelGGL(lane_scales, dim3((unsigned)sh.g), dim3(kScaleThreads), 0, stream, power,
-                     lane_energy, scale, lanes, len, w_ema);
+                     lane_energy, scale, lanes, len, w_from_end ? w_ema - 1.0f : w_ema,
+                     w_from_end);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   DecayArgs d{param, mantissa, gate, lr, wd, wd_dev};
