@@ -7,7 +7,9 @@
  *   1. twin-rail momentum in fp32: the fast rail lerps toward the gradient with weight
  *      1 - fast_beta, the slow rail with weight 1 - 0.98; the rails are blended as
  *      w * fast + (1 - w) * slow (w = fast_weight), and the gradient is lerped toward the blend
- *      with weight `momentum` (a Nesterov lookahead);
+ *      with weight `momentum` (a Nesterov lookahead).  Every lerp is torch's, which the page
+ *      calls: the difference of the end points, then one fused multiply-add about the nearer
+ *      end point (fma(w, end - start, start) for |w| < 1/2, else fma(w - 1, end - start, end));
  *   2. the lookahead is rounded to bf16, X;
  *   3. the Gram A = X^T X (rows > cols, "tall") or X X^T (otherwise) is formed in bf16; the trace
  *      of its bf16 diagonal is ||X||_F^2, giving d = sqrt(trace) * 1.05 + 1e-6; X and A are
@@ -20,8 +22,15 @@
  * Conventions for every entry point:
  *   - Pointers are DEVICE pointers to contiguous row-major data on the current HIP device.
  *     bf16 tensors are passed as their uint16_t bit patterns.
- *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue work: they never
- *     synchronise, and kernel faults surface at the caller's next synchronisation.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue work and return;
+ *     kernel faults surface at the caller's next synchronisation.  The exception is the cached
+ *     workspace of the entry points that take no workspace (anvil_bank_step, anvil_bank_update,
+ *     and anvil_bank_step_maps / anvil_bank_update_ws with a NULL workspace): the first call for
+ *     a shape larger than the cached buffer allocates (hipMalloc) and, when it replaces an older
+ *     buffer, synchronises the stream before freeing it.  Those calls therefore cannot be
+ *     captured into a HIP graph: on a capturing stream they return ANVIL_ERR_CAPTURING without
+ *     enqueueing anything.  Every entry point that takes a caller workspace allocates nothing,
+ *     never synchronises and may be captured.
  *   - g, m, n: stack size and matrix shape.  Any of them 0 means an empty stack: the call returns
  *     ANVIL_OK without touching memory (pointers may then be NULL).  Negative sizes are
  *     ANVIL_ERR_INVALID_ARG.  m and n must be multiples of 8 (16-byte rows), m*n <= 2^30,
@@ -52,7 +61,8 @@ enum anvil_status {
   ANVIL_ERR_MISALIGNED = 3,  /* a pointer is not 16-byte aligned */
   ANVIL_ERR_ALIAS = 4,       /* an output overlaps an input it may not overlap */
   ANVIL_ERR_OOM = 5,         /* the workspace allocation failed */
-  ANVIL_ERR_HIP = 6          /* a HIP API or launch error; see anvil_last_hip_error() */
+  ANVIL_ERR_HIP = 6,         /* a HIP API or launch error; see anvil_last_hip_error() */
+  ANVIL_ERR_CAPTURING = 7    /* a cached-workspace call on a stream that is being captured */
 };
 
 /* Gradient element types of the device-scalar entry points. */

@@ -20,6 +20,7 @@ ANVIL_ERR_MISALIGNED = 3
 ANVIL_ERR_ALIAS = 4
 ANVIL_ERR_OOM = 5
 ANVIL_ERR_HIP = 6
+ANVIL_ERR_CAPTURING = 7
 
 ANVIL_GRAD_F32 = 0
 ANVIL_GRAD_BF16 = 1

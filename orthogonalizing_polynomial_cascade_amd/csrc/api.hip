@@ -224,8 +224,14 @@ std::map<std::pair<int, hipStream_t>, std::pair<void*, size_t>> g_ws;
 // same stream from another thread that has to grow it waits until then, and its stream
 // synchronisation before the free then covers that work.
 int cached_workspace(size_t need, hipStream_t hs, char** out, std::unique_lock<std::mutex>* lock) {
+  // the cache may allocate, synchronise and free: none of that may happen under stream capture,
+  // and a captured graph would keep using a buffer the cache frees later
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(hs, &cs);
+  if (e != hipSuccess) return hip_status(e);
+  if (cs != hipStreamCaptureStatusNone) return ANVIL_ERR_CAPTURING;
   int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+  e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_status(e);
   *lock = std::unique_lock<std::mutex>(g_ws_mutex);
   auto& slot = g_ws[{dev, hs}];
@@ -294,6 +300,9 @@ const char* anvil_status_string(int status) {
     case ANVIL_ERR_ALIAS: return "an output overlaps an input";
     case ANVIL_ERR_OOM: return "workspace allocation failed";
     case ANVIL_ERR_HIP: return "HIP runtime or launch error (see anvil_last_hip_error)";
+    case ANVIL_ERR_CAPTURING:
+      return "the stream is being captured: pass a caller workspace (the cached workspace may "
+             "allocate and synchronise)";
     default: return "unknown status";
   }
 }

@@ -1,8 +1,9 @@
 // Frobenius normalisation of the cascade input.
 //
-// Source: modded-nanogpt anvil.py, `anvil_cascade`: the first Gram is taken on the unnormalised X,
-// the trace of its bf16 diagonal equals ||X||_F^2, and X and the Gram are rescaled by
-// d = sqrt(trace) * 1.05 + 1e-6 and d^2 instead of recomputing the Gram.
+// Source: modded-nanogpt anvil.py, `anvil_cascade`, the normalisation step after the first Gram.
+// The sum of a Gram matrix's diagonal is the squared Frobenius norm of X, so one Gram of the
+// unscaled X yields both the scale d = sqrt(trace) * 1.05 + 1e-6 and, divided by d^2, the Gram of
+// the scaled X that the first map needs.
 //
 // The trace arrives as per-diagonal-tile partial sums written by the map-0 Gram; each workgroup
 // sums them in slot order (deterministic), forms d in fp32, and rewrites its share of X and A in

@@ -96,8 +96,10 @@ def _mlp(w, t, g):
             P[i] = r.standard_normal((w.m, 32))
             Q[i] = r.standard_normal((32, w.n))
         return P, Q
-    P, Q = _fixed(w, "lowrank", lowrank)
-    low = 10.0 * np.matmul(P[:g], Q[:g]) / np.sqrt(32.0)
+    def low_part():
+        P, Q = _fixed(w, "lowrank", lowrank)
+        return 10.0 * np.matmul(P, Q) / np.sqrt(32.0)
+    low = _fixed(w, "low", low_part)[:g]
     z = _rng(4000 + t).standard_normal((g, w.m, w.n))
     return (z + low).astype(F32)
 

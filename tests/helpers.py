@@ -36,6 +36,87 @@ def rel_fro(got, want):
     return float(np.linalg.norm(got - want) / (den if den > 0 else 1.0))
 
 
+# The parity bars of the bf16 update and the fp32 rails.  The update bar is the relative Frobenius
+# error per matrix; on inputs whose normalised singular values lie far below the maps' window the
+# bf16 rounding noise is amplified and two correct accumulation orders of the oracle itself drift
+# apart, so there the bar is FLOOR_FACTOR times that measured drift, and an input whose drift
+# would put the bar above FLOOR_CAP fails outright (it is too ill-conditioned to tell a correct
+# implementation from a wrong one).
+OUT_TOL = 1e-2
+RAIL_TOL = 1e-6
+FLOOR_FACTOR = 1.5
+FLOOR_CAP = 2e-2
+
+
+def update_error(got, want, allow_nonfinite=False):
+    """Relative Frobenius error of one update matrix against the oracle's.
+
+    Every entry the oracle has finite must be finite on the GPU and vice versa (a NaN or Inf can
+    never hide behind a comparison that is False for NaN).  Unless allow_nonfinite, the oracle's
+    matrix must be finite throughout, so a diverged oracle cannot pass a comparison vacuously."""
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    assert got.shape == want.shape, (got.shape, want.shape)
+    fin = np.isfinite(want)
+    if not allow_nonfinite:
+        assert fin.all(), f"the oracle's matrix has {np.count_nonzero(~fin)} non-finite entries"
+    bad = np.isfinite(got) != fin
+    assert not bad.any(), f"{np.count_nonzero(bad)} entries finite on one side only"
+    if not fin.any():
+        return 0.0
+    r = rel_fro(got[fin], want[fin])
+    assert np.isfinite(r), r
+    return r
+
+
+def assert_update_close(got, want, floor_fn=None, what="update"):
+    """The parity bar on one matrix of the bf16 update.  floor_fn, when given, returns the relative
+    Frobenius drift between the oracle's fp32- and fp64-accumulation variants on the same input;
+    it is only evaluated when the error exceeds OUT_TOL.  Returns (error, bar used, floor or None)."""
+    r = update_error(got, want)
+    if r <= OUT_TOL:
+        return r, OUT_TOL, None
+    assert floor_fn is not None, f"{what}: relative Frobenius {r:.3e} above {OUT_TOL:.0e}"
+    floor = float(floor_fn())
+    assert np.isfinite(floor), f"{what}: noise floor {floor}"
+    tol = max(OUT_TOL, FLOOR_FACTOR * floor)
+    assert tol <= FLOOR_CAP, (f"{what}: noise floor {floor:.3e} puts the bar at {tol:.3e}, above "
+                              f"the cap {FLOOR_CAP:.0e}")
+    assert r <= tol, f"{what}: relative Frobenius {r:.3e} above {tol:.3e} (floor {floor:.3e})"
+    return r, tol, floor
+
+
+def assert_rails_close(got, want, what="rails"):
+    """fp32 rails within RAIL_TOL relative, element by element, with non-finite entries in the
+    same places (NaN-safe: the error of a NaN entry is never compared)."""
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    assert got.shape == want.shape, (got.shape, want.shape)
+    fin = np.isfinite(want)
+    assert np.array_equal(np.isfinite(got), fin), f"{what}: non-finite entries differ"
+    err = np.abs(got[fin] - want[fin]) / np.maximum(np.abs(want[fin]), 1e-30)
+    worst = float(err.max()) if err.size else 0.0
+    assert worst <= RAIL_TOL, f"{what}: relative error {worst:.2e}"
+    return worst
+
+
+def assert_sigma_band(out, what="update", band=0.3):
+    """Every singular value of one output matrix within `band` of 1."""
+    sv = np.linalg.svd(np.asarray(out, dtype=np.float64), compute_uv=False)
+    assert np.all(np.isfinite(sv)), what
+    assert np.all(np.abs(sv - 1.0) <= band), f"{what}: singular values in [{sv.min():.3f}, {sv.max():.3f}]"
+    return float(sv.min()), float(sv.max())
+
+
+def well_conditioned(x_bf16, lo=0.002):
+    """Every singular value of the normalised input (sigma / (1.05 ||X||_F)) at least lo: inside
+    the window of the six maps, where the composite map lands within 0.3 of 1."""
+    X = np.asarray(x_bf16, dtype=np.float64)
+    sv = np.linalg.svd(X, compute_uv=False)
+    d = np.sqrt(np.sum(X * X)) * 1.05
+    return bool(d > 0 and sv.min() / d >= lo)
+
+
 def assert_gemm_close(got, want, what, equal_frac=0.9):
     """A bf16 GEMM output against the oracle's: the two differ only in fp32 accumulation order, so
     the relative Frobenius error stays at bf16 rounding level, most entries are identical and no

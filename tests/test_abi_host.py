@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported_and_bound(lib):
 
 
 def test_status_strings(lib):
-    for code in range(7):
+    for code in range(8):
         s = lib.anvil_status_string(code)
         assert s and len(s) > 1
     assert lib.anvil_status_string(0) == b"ok"

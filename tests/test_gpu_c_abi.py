@@ -12,7 +12,7 @@ import pytest
 from oracle import anvil_oracle as O
 from orthogonalizing_polynomial_cascade_amd import anvil
 from orthogonalizing_polynomial_cascade_amd import workloads as W
-from tests.helpers import from_gpu, rel_fro, to_gpu_f32
+from tests.helpers import from_gpu, to_gpu_f32, update_error
 
 pytestmark = pytest.mark.gpu
 
@@ -61,5 +61,5 @@ def test_bank_step_from_c(gpu_lib, c_exe, tmp_path, g, m, n):
     out = (out_bits.astype(np.uint32) << 16).view(np.float32)
     want = O.cascade(O.R(y))
     for i in range(g):
-        assert rel_fro(out[i], want[i]) <= 1e-2, i
+        assert update_error(out[i], want[i]) <= 1e-2, i
     assert np.array_equal(from_gpu(v_py).view(np.uint32), v_want.view(np.uint32))

@@ -146,3 +146,38 @@ def test_bf16_gradient_full_size(gpu_lib, wname):
     gpu_lib.anvil_bank_step(to_gpu_f32(Gw), b["vel"], mu, fb, fw, out=b["out"], workspace=b["ws"])
     assert np.array_equal(bf16_bits_of(a["out"]), bf16_bits_of(b["out"]))
     assert torch.equal(a["vel"], b["vel"])
+
+
+def test_cached_workspace_refuses_capture(gpu_lib):
+    """The entry points without a workspace may allocate and synchronise, so on a capturing stream
+    they return ANVIL_ERR_CAPTURING and enqueue nothing; the caller-workspace form of the same
+    call captures and replays normally."""
+    import torch
+    g, m, n = 2, 200, 328
+    G = torch.randn((g, m, n), dtype=torch.float32, device="cuda")
+    vel = torch.zeros((2, g, m, n), dtype=torch.float32, device="cuda")
+    out = torch.empty((g, m, n), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(gpu_lib.workspace_bytes(g, m, n), dtype=torch.uint8, device="cuda")
+    # warm-up outside capture (kernel attributes are set on first launch)
+    gpu_lib.anvil_bank_step(G, vel.clone(), 0.95, 0.85, 1.0, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        graph.capture_begin()
+        try:
+            with pytest.raises(gpu_lib.AnvilError) as err:
+                gpu_lib.anvil_bank_step(G, vel, 0.95, 0.85, 1.0, out=out)
+            assert err.value.status == gpu_lib.ANVIL_ERR_CAPTURING
+            gpu_lib.anvil_bank_step(G, vel, 0.95, 0.85, 1.0, out=out, workspace=ws)
+        finally:
+            graph.capture_end()
+    torch.cuda.synchronize()
+    assert torch.equal(vel, torch.zeros_like(vel))      # nothing ran during capture
+    v_ref = torch.zeros_like(vel)
+    for _ in range(2):
+        graph.replay()
+        ref = gpu_lib.anvil_bank_step(G, v_ref, 0.95, 0.85, 1.0)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+        assert torch.equal(vel, v_ref)

@@ -1,29 +1,35 @@
 """The bank step with a caller-chosen map table (anvil_bank_step_maps) against the oracle's
 cascade with the same table: the page's cascade loop with another coefficient list and step count.
 
-Bars as for the bank step: relative Frobenius <= 1e-2 per matrix on the update (or 1.5x the
-oracle's own fp64/fp32-accumulation drift on inputs outside the maps' window), rails bit-exact."""
+Bars as for the bank step (tests/helpers.py): relative Frobenius <= 1e-2 per matrix on the
+update (or 1.5x the oracle's own fp64/fp32-accumulation drift on inputs outside the maps' window,
+capped at 2e-2), NaN-safe, with the oracle required to stay finite; rails bit-exact."""
 import numpy as np
 import pytest
 
 from oracle import anvil_oracle as O
 from orthogonalizing_polynomial_cascade_amd import workloads as W
-from tests.helpers import bf16_bits_of, from_gpu, rel_fro, to_gpu_f32
+from tests.helpers import assert_update_close, bf16_bits_of, from_gpu, rel_fro, to_gpu_f32
 
 pytestmark = pytest.mark.gpu
 
 NS5 = [(3.4445, -4.7750, 2.0315)] * 5
+# "anvil_ns3": the six ANVIL maps followed by five cubic Newton-Schulz steps 1.5 s - 0.5 s^3,
+# eleven maps in all (an odd count past the page's six).  The cubic step is contractive around 1,
+# so the longer table stays finite and does not amplify rounding noise (running the ANVIL table
+# twice would diverge: its first map sends 1 to about 1.73; following it with the quintic
+# Newton-Schulz steps raises the oracle's own accumulation-order drift to about 1.9e-2).
 TABLES = {"ns5": NS5, "anvil3": list(O.ANVIL_MAPS[:3]), "anvil1": list(O.ANVIL_MAPS[:1]),
-          "anvil_x2": list(O.ANVIL_MAPS) + list(O.ANVIL_MAPS)}
+          "anvil_ns3": list(O.ANVIL_MAPS) + [(1.5, -0.5, 0.0)] * 5}
 SHAPES = [(3, 200, 328), (3, 392, 136), (2, 264, 264), (2, 1096, 136), (1, 8, 16)]
 
 
 def _check(got, want_fn, X, g):
     for i in range(g):
-        r = rel_fro(got[i], want_fn(X[i:i + 1])[0])
-        if r > 1e-2:
-            floor = rel_fro(want_fn(X[i:i + 1], acc="fp32")[0], want_fn(X[i:i + 1])[0])
-            assert r <= 1.5 * floor, f"matrix {i}: {r:.3e} (floor {floor:.3e})"
+        x1 = X[i:i + 1]
+        assert_update_close(got[i], want_fn(x1)[0],
+                            lambda: rel_fro(want_fn(x1, acc="fp32")[0], want_fn(x1)[0]),
+                            f"matrix {i}")
 
 
 @pytest.mark.parametrize("name", list(TABLES))

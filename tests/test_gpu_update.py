@@ -13,13 +13,17 @@ import pytest
 
 from oracle import anvil_oracle as O
 from orthogonalizing_polynomial_cascade_amd import workloads as W
-from tests.helpers import bf16_bits_of, from_gpu, rel_fro, to_gpu_bf16, to_gpu_f32
+from tests.helpers import (assert_rails_close, assert_update_close, bf16_bits_of, from_gpu,
+                           rel_fro, to_gpu_bf16, to_gpu_f32, update_error)
 
 pytestmark = pytest.mark.gpu
 
 U = 2.0 ** -24
-OUT_TOL = 1e-2
-FLOOR_FACTOR = 1.5
+
+
+def _floor_fn(x1):
+    """The oracle's fp32- vs fp64-accumulation drift of the cascade on one bf16 input [1, m, n]."""
+    return lambda: rel_fro(O.cascade(x1, acc="fp32")[0], O.cascade(x1)[0])
 
 ROW_LANES = [(3, 392, 136), (2, 264, 264), (2, 1096, 136), (1, 8, 8), (2, 72, 8), (1, 1040, 1032),
              (1, 768, 256)]
@@ -68,7 +72,7 @@ def _check_equalizer(u, energy, beta2, out, e_gpu, p_gpu, s_gpu):
     # given the GPU's own bf16 scales the rescale is exact
     assert np.array_equal(out, O.R(u * s_gpu))
     want, _ = O.equalizer(u, energy, beta2)
-    assert rel_fro(out, want) <= 2.0 ** -7
+    assert update_error(out, want) <= 2.0 ** -7
 
 
 @pytest.mark.parametrize("g,m,n", ROW_LANES + COL_LANES)
@@ -176,7 +180,7 @@ def test_bank_update_composes_the_stages(gpu_lib, g, m, n):
         # the equalizer's outputs, checked as in the stage test (scales recovered from the output
         # are not available here, so compare with the oracle's scales at one bf16 ulp)
         want, e_or = O.equalizer(step_out, e_prev, 0.95)
-        assert rel_fro(out_gpu, want) <= 2.0 ** -7
+        assert update_error(out_gpu, want) <= 2.0 ** -7
         length = n if m >= n else m
         np.testing.assert_allclose(e_gpu, e_or, rtol=(length + 8) * U, atol=1e-30)
         p_want, m_want = O.decay_update(p, mant, out_gpu, wd, lr, from_gpu(vel)[1])
@@ -210,24 +214,20 @@ def test_bank_update_end_to_end(gpu_lib, g, m, n):
         u_or, v_or, e_or, p_or, m_or = O.bank_update(Gn, v_or, 0.95, 0.85, 1.0, e_or, 0.95, p_or,
                                                      m_or, wd, lr)
         u_or = O.bf16_to_f32(u_or)
-        v_gpu = from_gpu(vel)
-        assert np.max(np.abs(v_gpu - v_or) / np.maximum(np.abs(v_or), 1e-30)) <= 1e-6
-        tol = OUT_TOL
-        for i in range(g):
-            r = rel_fro(upd[i], u_or[i])
-            if r > OUT_TOL:
-                X = O.R(O.momentum_step(Gn[i:i + 1], v_prev[:, i:i + 1], 0.95, 0.85, 1.0)[1])
-                floor = rel_fro(O.cascade(X, acc="fp32")[0], O.cascade(X)[0])
-                tol = max(tol, FLOOR_FACTOR * floor)
-            assert r <= max(OUT_TOL, tol), f"step {t} matrix {i}: update {r:.3e}"
+        assert_rails_close(from_gpu(vel), v_or, f"step {t} rails")
         e_gpu = from_gpu(ed).reshape(e_or.shape)
-        assert rel_fro(e_gpu, e_or) <= 2 * tol
         master_gpu = ((bf16_bits_of(pd).astype(np.uint32) << 16) |
                       md.cpu().numpy().view(np.uint16)).view(np.float32)
         master_or = ((p_or.astype(np.uint32) << 16) | m_or).view(np.float32)
         d_gpu = master_gpu.astype(np.float64) - master_old
         d_or = master_or.astype(np.float64) - master_old
-        assert rel_fro(d_gpu, d_or) <= 2 * tol
+        for i in range(g):
+            # each matrix's own bar (its own noise floor where it needs one)
+            X = O.R(O.momentum_step(Gn[i:i + 1], v_prev[:, i:i + 1], 0.95, 0.85, 1.0)[1])
+            _, tol, _ = assert_update_close(upd[i], u_or[i], _floor_fn(X),
+                                            f"step {t} matrix {i} update")
+            assert update_error(e_gpu[i], e_or[i]) <= 2 * tol, f"step {t} matrix {i} energies"
+            assert update_error(d_gpu[i], d_or[i]) <= 2 * tol, f"step {t} matrix {i} master"
 
 
 def test_bank_update_workspace_variant_is_identical(gpu_lib):
@@ -278,15 +278,12 @@ def test_bank_update_full_size_sampled(gpu_lib, wname):
             G[i:i + 1], np.zeros((2, 1, m, n), np.float32), mu, fb, fw, e0, st.beta2,
             st.param_bits[i:i + 1], st.mantissa[i:i + 1], st.eff_wd, st.eff_lr[i:i + 1])
         u_or = O.bf16_to_f32(u_or)[0]
-        r = rel_fro(upd[i], u_or)
-        tol = OUT_TOL
-        if r > OUT_TOL:
-            X = O.R(O.momentum_step(G[i:i + 1], np.zeros((2, 1, m, n), np.float32), mu, fb, fw)[1])
-            tol = max(OUT_TOL, FLOOR_FACTOR * rel_fro(O.cascade(X, acc="fp32")[0], O.cascade(X)[0]))
-        assert r <= tol, f"matrix {i}: update {r:.3e} > {tol:.3e}"
-        assert rel_fro(e_gpu[i], e_or.reshape(lanes)) <= 2 * tol
+        X = O.R(O.momentum_step(G[i:i + 1], np.zeros((2, 1, m, n), np.float32), mu, fb, fw)[1])
+        _, tol, _ = assert_update_close(upd[i], u_or, _floor_fn(X), f"matrix {i} update")
+        assert update_error(e_gpu[i], e_or.reshape(lanes)) <= 2 * tol, f"matrix {i} energies"
         master_old = ((st.param_bits[i].astype(np.uint32) << 16) | st.mantissa[i]).view(np.float32)
         master_gpu = ((p_gpu[i].astype(np.uint32) << 16) | m_gpu[i]).view(np.float32)
         master_or = ((p_or[0].astype(np.uint32) << 16) | m_or[0]).view(np.float32)
-        assert rel_fro(master_gpu.astype(np.float64) - master_old,
-                       master_or.astype(np.float64) - master_old) <= 2 * tol
+        assert update_error(master_gpu.astype(np.float64) - master_old,
+                            master_or.astype(np.float64) - master_old) <= 2 * tol, \
+            f"matrix {i} master"

@@ -187,6 +187,9 @@ def test_noise_floor_of_warmed_mlp_input():
 # odd-length prefix of the ANVIL table: the closed form holds for any list of maps.
 NS5 = [(3.4445, -4.7750, 2.0315)] * 5
 ANVIL3 = list(O.ANVIL_MAPS[:3])
+# The six ANVIL maps followed by five cubic Newton-Schulz steps p(s) = 1.5 s - 0.5 s^3 (c = 0):
+# eleven maps, past the page's six, that stay bounded (the cubic step is contractive around 1).
+ANVIL_NS3 = list(O.ANVIL_MAPS) + [(1.5, -0.5, 0.0)] * 5
 
 
 def _F_of(maps, s):
@@ -196,7 +199,7 @@ def _F_of(maps, s):
     return s
 
 
-@pytest.mark.parametrize("maps", [NS5, ANVIL3], ids=["ns5", "anvil3"])
+@pytest.mark.parametrize("maps", [NS5, ANVIL3, ANVIL_NS3], ids=["ns5", "anvil3", "anvil_ns3"])
 @pytest.mark.parametrize("shape", [(8, 24), (24, 8), (16, 16), (48, 32)])
 def test_exact_mode_with_other_map_tables(maps, shape):
     rng = np.random.default_rng(3 * sum(shape))
@@ -247,3 +250,13 @@ def test_permuted_diagonal_is_exact_scalar_cascade(m, n):
     assert np.array_equal(out[rows, cols], want_cls[cls])
     assert np.count_nonzero(out) == s
     assert len(set(want_cls.tolist())) == 3   # the three classes stay distinguishable
+
+
+def test_anvil_ns3_table_converges():
+    """After the ANVIL maps every singular value of the window is within 0.3 of 1; the cubic
+    Newton-Schulz steps then pull it to 1 quadratically (its derivative vanishes at 1)."""
+    s = np.linspace(0.003, 0.95, 4001)
+    f6 = _F_of(list(O.ANVIL_MAPS), s)
+    f11 = _F_of(ANVIL_NS3, s)
+    assert np.all(np.abs(f6 - 1) <= 0.3)
+    assert np.all(np.abs(f11 - 1) <= 1e-6)

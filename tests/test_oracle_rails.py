@@ -41,7 +41,8 @@ def test_engage_schedule():
 
 def test_pre_engage_ignores_slow_rail_but_updates_it():
     """With fast weight 1 the blend is the fast rail exactly, so the lookahead does not depend on
-    the slow rail at all; the slow rail still moves (it accumulates from step 0)."""
+    the slow rail at all; the slow rail still moves (it is updated at every step, engaged or
+    not)."""
     rng = np.random.default_rng(2)
     G = rng.standard_normal((1, 16, 8)).astype(np.float32)
     v = rng.standard_normal((2, 1, 16, 8)).astype(np.float32)
