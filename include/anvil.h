@@ -62,7 +62,8 @@ enum anvil_status {
   ANVIL_ERR_ALIAS = 4,       /* an output overlaps an input it may not overlap */
   ANVIL_ERR_OOM = 5,         /* the workspace allocation failed */
   ANVIL_ERR_HIP = 6,         /* a HIP API or launch error; see anvil_last_hip_error() */
-  ANVIL_ERR_CAPTURING = 7    /* a cached-workspace call on a stream that is being captured */
+  ANVIL_ERR_CAPTURING = 7,   /* a cached-workspace call on a stream that is being captured */
+  ANVIL_ERR_TOO_LARGE = 8    /* anvil_bank_step_noalloc: the step needs more than its scratch */
 };
 
 /* Gradient element types of the device-scalar entry points. */
@@ -106,6 +107,23 @@ int anvil_bank_step(const float* grad, float* velocity, float momentum, float fa
 int anvil_bank_step_ws(const float* grad, float* velocity, float momentum, float fast_beta,
                        float fast_weight, uint16_t* out, int64_t g, int64_t m, int64_t n,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device scratch that anvil_bank_step_noalloc holds per device (192 MiB: every bank of
+ * the qk, vo, mlp, Vs and Us shapes fits, the largest, 32 x 4096 x 512, needs 161 MiB). */
+#define ANVIL_NOALLOC_SCRATCH_BYTES ((size_t)192 << 20)
+
+/* As anvil_bank_step, for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  The workspace is a device
+ * array of ANVIL_NOALLOC_SCRATCH_BYTES compiled into the library, one per device, held until the
+ * process ends; the call allocates nothing and never synchronises.  A bank whose
+ * anvil_workspace_bytes(g, m, n) exceeds ANVIL_NOALLOC_SCRATCH_BYTES is refused with
+ * ANVIL_ERR_TOO_LARGE before anything is enqueued.  Every call on a device shares that device's
+ * scratch: calls that may overlap in time on one device (other streams, other threads) race and
+ * must be ordered by the caller.  The first call on a device looks up the scratch's address
+ * (hipGetSymbolAddress), so make it outside graph capture. */
+int anvil_bank_step_noalloc(const float* grad, float* velocity, float momentum, float fast_beta,
+                            float fast_weight, uint16_t* out, int64_t g, int64_t m, int64_t n,
+                            void* stream);
 
 /* The bank step with a caller-chosen table of quintic maps (the page's cascade loop with another
  * coefficient list and step count, e.g. a plain quintic Newton-Schulz iteration).

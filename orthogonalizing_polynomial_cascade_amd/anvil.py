@@ -21,6 +21,8 @@ ANVIL_ERR_ALIAS = 4
 ANVIL_ERR_OOM = 5
 ANVIL_ERR_HIP = 6
 ANVIL_ERR_CAPTURING = 7
+ANVIL_ERR_TOO_LARGE = 8
+NOALLOC_SCRATCH_BYTES = 192 << 20   # ANVIL_NOALLOC_SCRATCH_BYTES of include/anvil.h
 
 ANVIL_GRAD_F32 = 0
 ANVIL_GRAD_BF16 = 1
@@ -34,6 +36,7 @@ SIGNATURES = {
     "anvil_version": (_i, []),
     "anvil_bank_step": (_i, [_vp, _vp, _f, _f, _f, _vp, _i64, _i64, _i64, _vp]),
     "anvil_bank_step_ws": (_i, [_vp, _vp, _f, _f, _f, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),
+    "anvil_bank_step_noalloc": (_i, [_vp, _vp, _f, _f, _f, _vp, _i64, _i64, _i64, _vp]),
     "anvil_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "anvil_release_workspaces": (_i, []),
     "anvil_momentum": (_i, [_vp, _vp, _f, _f, _f, _vp, _i64, _i64, _i64, _vp]),
@@ -164,6 +167,22 @@ def anvil_bank_step(grad, velocity, momentum, fast_beta, fast_weight, out=None, 
                                     _ptr(out), g, m, n, _ptr(workspace), workspace.numel(),
                                     _stream(stream))
         _check("anvil_bank_step_ws", st)
+    return out
+
+
+def anvil_bank_step_noalloc(grad, velocity, momentum, fast_beta, fast_weight, out, stream=None):
+    """anvil_bank_step with the library's built-in device scratch: the C call allocates nothing.
+    `out` (bf16 [g, m, n]) must be given; the bank's workspace_bytes(g, m, n) may be at most
+    NOALLOC_SCRATCH_BYTES.  Calls on one device share that scratch (order them)."""
+    import torch
+    lib = load()
+    _need(grad, "grad", torch.float32)
+    g, m, n = _gmn(grad)
+    _need(velocity, "velocity", torch.float32, (2, g, m, n))
+    _need(out, "out", torch.bfloat16, (g, m, n))
+    _check("anvil_bank_step_noalloc", lib.anvil_bank_step_noalloc(
+        _ptr(grad), _ptr(velocity), momentum, fast_beta, fast_weight, _ptr(out), g, m, n,
+        _stream(stream)))
     return out
 
 

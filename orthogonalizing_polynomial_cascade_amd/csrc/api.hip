@@ -2,6 +2,7 @@
 // ANVIL bank step (modded-nanogpt anvil.py, `anvil_cascade`).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <initializer_list>
 #include <map>
 #include <mutex>
@@ -279,6 +280,35 @@ int pick_workspace(void* workspace, size_t workspace_bytes, const Shape& sh, hip
   return cached_workspace(layout_for(sh).total, hs, ws, lock);
 }
 
+// Scratch of anvil_bank_step_noalloc: the whole workspace of one bank step in a file-scope device
+// array, so that a call allocates nothing.  Each device the library runs on holds its own copy
+// (ANVIL_NOALLOC_SCRATCH_BYTES) until the process ends.  In host code `scratch` only names the
+// symbol; its device address comes from hipGetSymbolAddress, once per device, and every launch
+// uses that address.
+static __device__ __align__(256) char scratch[ANVIL_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<char*> g_scratch_addr[kMaxScratchDevices];
+
+// The current device's address of `scratch` (looked up on the first call on that device).
+int scratch_address(char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxScratchDevices) return ANVIL_ERR_UNSUPPORTED;
+  char* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    void* addr = nullptr;
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (addr == nullptr) return ANVIL_ERR_HIP;
+    p = static_cast<char*>(addr);
+    g_scratch_addr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return ANVIL_OK;
+}
+
 MomentumIn by_value(const float* grad, float momentum, float fast_beta, float fast_weight) {
   return MomentumIn{grad, false, nullptr, momentum, fast_beta, fast_weight};
 }
@@ -300,6 +330,9 @@ const char* anvil_status_string(int status) {
     case ANVIL_ERR_ALIAS: return "an output overlaps an input";
     case ANVIL_ERR_OOM: return "workspace allocation failed";
     case ANVIL_ERR_HIP: return "HIP runtime or launch error (see anvil_last_hip_error)";
+    case ANVIL_ERR_TOO_LARGE:
+      return "the bank step needs more scratch than anvil_bank_step_noalloc holds "
+             "(anvil_workspace_bytes(g, m, n) > ANVIL_NOALLOC_SCRATCH_BYTES)";
     case ANVIL_ERR_CAPTURING:
       return "the stream is being captured: pass a caller workspace (the cached workspace may "
              "allocate and synchronise)";
@@ -353,6 +386,25 @@ int anvil_bank_step(const float* grad, float* velocity, float momentum, float fa
   st = cached_workspace(layout_for(sh).total, hs, &ws, &lock);
   if (st != ANVIL_OK) return st;
   return run_step(by_value(grad, momentum, fast_beta, fast_weight), velocity, out, sh, ws, hs);
+}
+
+int anvil_bank_step_noalloc(const float* grad, float* velocity, float momentum, float fast_beta,
+                            float fast_weight, uint16_t* out, int64_t g, int64_t m, int64_t n,
+                            void* stream) {
+  Shape sh;
+  bool empty = false;
+  int st = check_shape(g, m, n, &sh, &empty);
+  if (st != ANVIL_OK || empty) return st;
+  st = check_step_args(grad, 4, velocity, out, sh);
+  if (st != ANVIL_OK) return st;
+  if (layout_for(sh).total > ANVIL_NOALLOC_SCRATCH_BYTES) return ANVIL_ERR_TOO_LARGE;
+  char* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != ANVIL_OK) return st;
+  // every scratch region the step reads is written earlier in the same step (ping-pong copy,
+  // A, B, trace partials, d), so the array needs no clearing between calls
+  return run_step(by_value(grad, momentum, fast_beta, fast_weight), velocity, out, sh, ws,
+                  static_cast<hipStream_t>(stream));
 }
 
 int anvil_bank_step_maps(const float* grad, float* velocity, float momentum, float fast_beta,

@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported_and_bound(lib):
 
 
 def test_status_strings(lib):
-    for code in range(8):
+    for code in range(9):
         s = lib.anvil_status_string(code)
         assert s and len(s) > 1
     assert lib.anvil_status_string(0) == b"ok"
@@ -250,3 +250,21 @@ def test_device_scalar_entry_points_checks(lib):
     assert lib.anvil_bank_update_dev(*args, W, need - 1, None) == anvil.ANVIL_ERR_UNSUPPORTED
     assert lib.anvil_bank_update_dev(A, 1, B, E + 8, C, D, 0.95, E, F, L, 2, 64, 32, W, need,
                                      None) == anvil.ANVIL_ERR_ALIAS
+
+
+def test_noalloc_refuses_oversized_banks_on_the_host(lib):
+    """anvil_bank_step_noalloc checks its scratch limit before any HIP call: a bank needing more
+    than ANVIL_NOALLOC_SCRATCH_BYTES is refused with ANVIL_ERR_TOO_LARGE (fake, disjoint
+    addresses; nothing is dereferenced), the usual argument checks still come first."""
+    far = [0x1000000000, 0x2000000000, 0x3000000000]
+    g, m, n = 48, 2816, 768
+    assert lib.anvil_workspace_bytes(g, m, n) > anvil.NOALLOC_SCRATCH_BYTES
+    assert lib.anvil_workspace_bytes(24, m, n) <= anvil.NOALLOC_SCRATCH_BYTES
+    assert lib.anvil_bank_step_noalloc(far[0], far[1], 0.95, 0.85, 1.0, far[2], g, m, n,
+                                       None) == anvil.ANVIL_ERR_TOO_LARGE
+    assert lib.anvil_bank_step_noalloc(far[0], far[1], 0.95, 0.85, 1.0, None, g, m, n,
+                                       None) == anvil.ANVIL_ERR_INVALID_ARG
+    assert lib.anvil_bank_step_noalloc(far[0], far[0], 0.95, 0.85, 1.0, far[2], 2, 64, 32,
+                                       None) == anvil.ANVIL_ERR_ALIAS
+    assert lib.anvil_bank_step_noalloc(None, None, 0.95, 0.85, 1.0, None, 0, 64, 32, None) == 0
+    assert lib.anvil_status_string(anvil.ANVIL_ERR_TOO_LARGE).startswith(b"the bank step needs")
