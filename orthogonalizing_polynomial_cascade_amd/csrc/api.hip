@@ -94,7 +94,7 @@ Layout layout_for(const Shape& sh) {
   l.b = off;
   off += round_up(g * s * s * 2);
   l.partials = off;
-  off += round_up(g * anvil::gram_trace_slots(sh.s()) * 4);
+  off += round_up(g * anvil::gram_trace_slots(sh) * 4);
   l.d = off;
   off += round_up(g * 4);
   l.lanes = off;   // equalizer scratch: lane powers and lane scales
@@ -617,7 +617,7 @@ int64_t anvil_trace_slots(int64_t m, int64_t n) {
   Shape sh;
   bool empty = false;
   if (check_shape(1, m, n, &sh, &empty) != ANVIL_OK || empty) return 0;
-  return anvil::gram_trace_slots(sh.s());
+  return anvil::gram_trace_slots(sh);
 }
 
 int anvil_gram(const uint16_t* x, uint16_t* a_out, float* trace_partials, int64_t g, int64_t m,
@@ -631,7 +631,7 @@ int anvil_gram(const uint16_t* x, uint16_t* a_out, float* trace_partials, int64_
     return ANVIL_ERR_MISALIGNED;
   const size_t s = sh.s();
   const size_t xb = static_cast<size_t>(sh.g) * sh.m * sh.n * 2, ab = sh.g * s * s * 2;
-  const size_t tb = static_cast<size_t>(sh.g) * anvil::gram_trace_slots(sh.s()) * 4;
+  const size_t tb = static_cast<size_t>(sh.g) * anvil::gram_trace_slots(sh) * 4;
   if (overlap(a_out, ab, x, xb) || (trace_partials && (overlap(trace_partials, tb, x, xb) ||
                                                        overlap(trace_partials, tb, a_out, ab))))
     return ANVIL_ERR_ALIAS;
@@ -651,7 +651,7 @@ int anvil_normalize(uint16_t* x, uint16_t* a, const float* trace_partials, float
     return ANVIL_ERR_MISALIGNED;
   const size_t s = sh.s();
   const size_t xb = static_cast<size_t>(sh.g) * sh.m * sh.n * 2, ab = sh.g * s * s * 2;
-  const size_t tb = static_cast<size_t>(sh.g) * anvil::gram_trace_slots(sh.s()) * 4;
+  const size_t tb = static_cast<size_t>(sh.g) * anvil::gram_trace_slots(sh) * 4;
   if (overlap(x, xb, a, ab) || overlap(x, xb, trace_partials, tb) || overlap(a, ab, trace_partials, tb) ||
       (d_out && (overlap(d_out, sh.g * 4, x, xb) || overlap(d_out, sh.g * 4, a, ab) ||
                  overlap(d_out, sh.g * 4, trace_partials, tb))))

@@ -647,6 +647,13 @@ hipError_t launch(GemmParams p, int64_t g, hipStream_t stream) {
 //    small stacks.  The wave layout and ring depth change no arithmetic: an element's MFMA chain
 //    over k and its epilogue are the same in every configuration.
 constexpr int kSymTile = 128;
+// Small Grams (at most 256 rows) take 64x64 tiles: such launches have few tiles (three per
+// 256x768 matrix at 128x128) and each workgroup streams its operands at a limited rate, so
+// smaller tiles that spread the same work over more workgroups finish sooner.  The Gram of a
+// tall matrix reads X down its columns (K-major slabs of at least 128 rows) and keeps 128x128.
+constexpr int kSmallSym = 256;
+int gram_tile(const Shape& sh) { return (!sh.tall() && sh.s() <= kSmallSym) ? 64 : kSymTile; }
+int poly_tile(int s) { return s <= kSmallSym ? 64 : kSymTile; }
 // The Gram (K = the long side, up to thousands) sums each group of 8 slabs (512 k) in fresh
 // registers and adds the group sums to the running sums: on low-rank-dominated inputs one long
 // MFMA accumulation chain drifts from an fp64 reference noticeably more than fp32 sgemm does,
@@ -657,10 +664,11 @@ constexpr int kSymTile = 128;
 #endif
 constexpr int kGramSlabGroup = ANVIL_SLAB_GROUP;
 constexpr int kFullRound = 512;
+constexpr int kCus = 256;
 
 }  // namespace
 
-int gram_trace_slots(int s) { return ceil_div(s, kSymTile); }
+int gram_trace_slots(const Shape& sh) { return ceil_div(sh.s(), gram_tile(sh)); }
 
 hipError_t launch_gram(const uint16_t* x, uint16_t* a, float* trace_partials, const Shape& sh,
                        hipStream_t stream) {
@@ -677,9 +685,11 @@ hipError_t launch_gram(const uint16_t* x, uint16_t* a, float* trace_partials, co
   p.strideC = (int64_t)s * s;
   p.ldc = s;
   p.trace = trace_partials;
-  p.trace_slots = gram_trace_slots(s);
-  p.tiles_m = p.tiles_n = ceil_div(s, kSymTile);
+  p.trace_slots = gram_trace_slots(sh);
+  p.tiles_m = p.tiles_n = ceil_div(s, gram_tile(sh));
   p.tiles = p.tiles_m * (p.tiles_m + 1) / 2;
+  if (gram_tile(sh) == 64)
+    return launch<OP_GRAM, false, false, 64, 64, 2, 2, 2, 64, kGramSlabGroup>(p, sh.g, stream);
   if (sh.tall())
     return launch<OP_GRAM, true, true, 128, 128, 2, 2, 2, 64, kGramSlabGroup>(p, sh.g, stream);
   return launch<OP_GRAM, false, false, 128, 128, 2, 2, 2, 64, kGramSlabGroup>(p, sh.g, stream);
@@ -702,8 +712,10 @@ hipError_t launch_poly(const uint16_t* a, uint16_t* bout, float coef_b, float co
   p.lde = s;
   p.alpha = coef_b;
   p.beta = coef_c;
-  p.tiles_m = p.tiles_n = ceil_div(s, kSymTile);
+  p.tiles_m = p.tiles_n = ceil_div(s, poly_tile(s));
   p.tiles = p.tiles_m * (p.tiles_m + 1) / 2;
+  if (poly_tile(s) == 64)
+    return launch<OP_POLY, false, false, 64, 64, 2, 2, 2, 64, 0>(p, g, stream);
   return launch<OP_POLY, false, false, 128, 128, 2, 4, 2, 64, 0>(p, g, stream);
 }
 
@@ -758,6 +770,9 @@ hipError_t launch_apply(const uint16_t* x, const uint16_t* bm, uint16_t* c, floa
   const int64_t wide_tiles = (int64_t)ceil_div(sh.m, 128) * ceil_div(sh.n, 256) * sh.g;
   if (2 * wide_tiles >= kFullRound)
     return launch_apply_cfg<128, 256, 2, 4, 2, 32>(x, bm, c, coef_a, split, sh, stream);
+  // launches with no more 128x128 tiles than CUs: 64x128 tiles, twice the workgroups
+  if ((int64_t)ceil_div(sh.m, 128) * ceil_div(sh.n, 128) * sh.g <= kCus)
+    return launch_apply_cfg<64, 128, 2, 2, 2, 64>(x, bm, c, coef_a, split, sh, stream);
   return launch_apply_cfg<128, 128, 2, 4, 2, 64>(x, bm, c, coef_a, split, sh, stream);
 }
 

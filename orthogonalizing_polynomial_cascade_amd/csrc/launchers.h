@@ -27,7 +27,7 @@ struct Shape {
 };
 
 // Number of diagonal tiles of the Gram (trace partials per matrix).
-int gram_trace_slots(int s);
+int gram_trace_slots(const Shape& sh);
 
 hipError_t launch_gram(const uint16_t* x, uint16_t* a, float* trace_partials, const Shape& sh,
                        hipStream_t stream);

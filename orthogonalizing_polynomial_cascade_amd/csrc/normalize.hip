@@ -63,7 +63,7 @@ hipError_t launch_normalize(uint16_t* x, uint16_t* a, const float* trace_partial
   hipLaunchKernelGGL(normalize_kernel, dim3((unsigned)blocks, (unsigned)sh.g), dim3(256), 0,
                      stream, reinterpret_cast<u32x4_t*>(x), x_chunks,
                      reinterpret_cast<u32x4_t*>(a), a_chunks, trace_partials,
-                     gram_trace_slots(s), d);
+                     gram_trace_slots(sh), d);
   return hipGetLastError();
 }
 
