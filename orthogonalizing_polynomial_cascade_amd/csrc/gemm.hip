@@ -647,13 +647,14 @@ hipError_t launch(GemmParams p, int64_t g, hipStream_t stream) {
 //    small stacks.  The wave layout and ring depth change no arithmetic: an element's MFMA chain
 //    over k and its epilogue are the same in every configuration.
 constexpr int kSymTile = 128;
-// Small Grams (at most 256 rows) take 64x64 tiles: such launches have few tiles (three per
-// 256x768 matrix at 128x128) and each workgroup streams its operands at a limited rate, so
-// smaller tiles that spread the same work over more workgroups finish sooner.  The Gram of a
-// tall matrix reads X down its columns (K-major slabs of at least 128 rows) and keeps 128x128.
+// Small Grams and polynomials (at most 256 rows) take 32x32 tiles, one wave each: such launches
+// have few tiles (three per 256x768 matrix at 128x128) and each workgroup streams its operands at
+// a limited rate, so smaller tiles that spread the same work over more workgroups finish sooner.
+// The Gram of a tall matrix reads X down its columns (K-major slabs of at least 128 rows) and
+// keeps 128x128.
 constexpr int kSmallSym = 256;
-int gram_tile(const Shape& sh) { return (!sh.tall() && sh.s() <= kSmallSym) ? 64 : kSymTile; }
-int poly_tile(int s) { return s <= kSmallSym ? 64 : kSymTile; }
+int gram_tile(const Shape& sh) { return (!sh.tall() && sh.s() <= kSmallSym) ? 32 : kSymTile; }
+int poly_tile(int s) { return s <= kSmallSym ? 32 : kSymTile; }
 // The Gram (K = the long side, up to thousands) sums each group of 8 slabs (512 k) in fresh
 // registers and adds the group sums to the running sums: on low-rank-dominated inputs one long
 // MFMA accumulation chain drifts from an fp64 reference noticeably more than fp32 sgemm does,
@@ -688,8 +689,8 @@ hipError_t launch_gram(const uint16_t* x, uint16_t* a, float* trace_partials, co
   p.trace_slots = gram_trace_slots(sh);
   p.tiles_m = p.tiles_n = ceil_div(s, gram_tile(sh));
   p.tiles = p.tiles_m * (p.tiles_m + 1) / 2;
-  if (gram_tile(sh) == 64)
-    return launch<OP_GRAM, false, false, 64, 64, 2, 2, 2, 64, kGramSlabGroup>(p, sh.g, stream);
+  if (gram_tile(sh) == 32)
+    return launch<OP_GRAM, false, false, 32, 32, 1, 1, 2, 64, kGramSlabGroup>(p, sh.g, stream);
   if (sh.tall())
     return launch<OP_GRAM, true, true, 128, 128, 2, 2, 2, 64, kGramSlabGroup>(p, sh.g, stream);
   return launch<OP_GRAM, false, false, 128, 128, 2, 2, 2, 64, kGramSlabGroup>(p, sh.g, stream);
@@ -714,8 +715,8 @@ hipError_t launch_poly(const uint16_t* a, uint16_t* bout, float coef_b, float co
   p.beta = coef_c;
   p.tiles_m = p.tiles_n = ceil_div(s, poly_tile(s));
   p.tiles = p.tiles_m * (p.tiles_m + 1) / 2;
-  if (poly_tile(s) == 64)
-    return launch<OP_POLY, false, false, 64, 64, 2, 2, 2, 64, 0>(p, g, stream);
+  if (poly_tile(s) == 32)
+    return launch<OP_POLY, false, false, 32, 32, 1, 1, 2, 64, 0>(p, g, stream);
   return launch<OP_POLY, false, false, 128, 128, 2, 4, 2, 64, 0>(p, g, stream);
 }
 
@@ -770,9 +771,9 @@ hipError_t launch_apply(const uint16_t* x, const uint16_t* bm, uint16_t* c, floa
   const int64_t wide_tiles = (int64_t)ceil_div(sh.m, 128) * ceil_div(sh.n, 256) * sh.g;
   if (2 * wide_tiles >= kFullRound)
     return launch_apply_cfg<128, 256, 2, 4, 2, 32>(x, bm, c, coef_a, split, sh, stream);
-  // launches with no more 128x128 tiles than CUs: 64x128 tiles, twice the workgroups
+  // launches with no more 128x128 tiles than CUs: 32x128 tiles, four times the workgroups
   if ((int64_t)ceil_div(sh.m, 128) * ceil_div(sh.n, 128) * sh.g <= kCus)
-    return launch_apply_cfg<64, 128, 2, 2, 2, 64>(x, bm, c, coef_a, split, sh, stream);
+    return launch_apply_cfg<32, 128, 1, 2, 2, 64>(x, bm, c, coef_a, split, sh, stream);
   return launch_apply_cfg<128, 128, 2, 4, 2, 64>(x, bm, c, coef_a, split, sh, stream);
 }
 

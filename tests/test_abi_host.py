@@ -118,11 +118,11 @@ def test_workspace_size_and_trace_slots(lib):
     assert ws >= g * m * n * 2 + 2 * g * s * s * 2 + g * 4
     assert ws % 256 == 0
     assert lib.anvil_trace_slots(2816, 768) >= 1
-    # one partial per diagonal tile of the Gram: 128x128 tiles, or 64x64 for Grams of at most
+    # one partial per diagonal tile of the Gram: 128x128 tiles, or 32x32 for Grams of at most
     # 256 rows read along the rows (wide and square matrices)
     assert lib.anvil_trace_slots(2816, 768) == 6
     assert lib.anvil_trace_slots(768, 256) == 2
-    assert lib.anvil_trace_slots(256, 768) == 4
+    assert lib.anvil_trace_slots(256, 768) == 8
     assert lib.anvil_trace_slots(264, 264) == 3
     assert lib.anvil_trace_slots(7, 8) == 0
 
