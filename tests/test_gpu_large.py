@@ -8,7 +8,8 @@ import pytest
 
 from oracle import anvil_oracle as O
 from orthogonalizing_polynomial_cascade_amd import workloads as W
-from tests.helpers import assert_gemm_close, from_gpu, sigma_classes, to_gpu_f32
+from tests.helpers import (assert_gemm_close, bf16_bits_of, from_gpu, sigma_classes, to_gpu_f32,
+                           update_error)
 
 pytestmark = pytest.mark.gpu
 
@@ -177,3 +178,28 @@ def test_row_lanes_beyond_the_grid_cap(gpu_lib):
     power = (u.astype(np.float64) ** 2).mean(axis=-1, keepdims=True)
     energy = (power * np.exp(rng.standard_normal(power.shape))).astype(np.float32)
     _check_equalizer(u, energy, 0.95, *_gpu_equalize(gpu_lib, u, energy, 0.95))
+
+
+@pytest.mark.parametrize("m,n", [(8, 16), (16, 8)])
+def test_max_stack_count(gpu_lib, m, n):
+    """The largest stack count the ABI takes (65535 matrices): every kernel's grid spans the
+    whole stack.  Sampled matrices (first, middle, last) against the oracle, the rails bit for bit,
+    and a matrix stepped alone equal to its slice of the stack."""
+    import torch
+    g = 65535
+    G = W.gaussian(g, m, n, seed=61).grad(0)
+    vel = torch.zeros((2, g, m, n), dtype=torch.float32, device="cuda")
+    out = gpu_lib.anvil_bank_step(to_gpu_f32(G), vel, 0.95, 0.85, 0.4385)
+    torch.cuda.synchronize()
+    got = from_gpu(out)
+    v_gpu = from_gpu(vel)
+    for i in (0, g // 2, g - 1):
+        v_or, y = O.momentum_step(G[i:i + 1], np.zeros((2, 1, m, n), np.float32), 0.95, 0.85,
+                                  0.4385)
+        assert np.array_equal(v_gpu[:, i:i + 1].view(np.uint32), v_or.view(np.uint32))
+        want = O.cascade(O.R(y))[0]
+        assert update_error(got[i], want) <= 1e-2, i
+        one = gpu_lib.anvil_bank_step(to_gpu_f32(G[i:i + 1]),
+                                      torch.zeros((2, 1, m, n), dtype=torch.float32,
+                                                  device="cuda"), 0.95, 0.85, 0.4385)
+        assert np.array_equal(bf16_bits_of(one)[0], bf16_bits_of(out[i:i + 1])[0]), i
