@@ -354,6 +354,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
     }
   };
 
+  // On a diagonal tile of a symmetric product, a wave whose block lies wholly below the diagonal
+  // stores nothing (those entries come from the mirror of the block above it): it takes its share
+  // of the copies and every barrier, but skips its fragment reads and multiplies.
+  const bool idle = (OP != OP_APPLY) && ti == tj && wm * C::kWTM >= (wn + 1) * C::kWTN;
+
   f32x16_t slab[SLAB > 0 ? C::kFM : 1][SLAB > 0 ? C::kFN : 1];
   for (int kt = 0; kt < KT; ++kt) {
     // slab kt has landed once at most STAGES-2 younger slabs of this wave are still in flight
@@ -374,6 +379,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
     if constexpr (kHasE) {
       if (kt == KT - 1) load_e(ecur, 0);
     }
+    if (idle) continue;
     const char* tp = smem + (kt % STAGES) * C::kStageBytes;
     const char* tq = tp + C::kQOffset;
 
