@@ -399,25 +399,39 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
             for (int r = 0; r < 16; ++r) slab[fm][fn][r] = 0.0f;
       }
     }
+    // Fragments of the whole slab are read before its multiplies when a wave holds at most two
+    // fragments (its MFMAs then form one or two dependent chains, and reading per k-step would
+    // put an LDS round trip in front of every MFMA); larger wave tiles read per k-step, which
+    // keeps their registers within the two workgroups per CU (reading ahead there made the
+    // 128x256 apply 140 registers and the mlp step 25% slower).
+    constexpr bool kHoist = C::kFM * C::kFN <= 2;
+    constexpr int kKs = BK / 16;
+    bf16x8_t fa[kKs][C::kFM], fb[kKs][C::kFN];
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8_t fa[C::kFM], fb[C::kFN];
+    for (int ks = 0; ks < kKs; ++ks) {
+      if (ks == 0 || !kHoist) {
 #pragma unroll
-      for (int fm = 0; fm < C::kFM; ++fm)
-        fa[fm] = read_frag<PT, BM, BK>(tp, wm * C::kWTM + fm * 32, ks, lane);
+        for (int kr = ks; kr < (kHoist ? kKs : ks + 1); ++kr) {
 #pragma unroll
-      for (int fn = 0; fn < C::kFN; ++fn)
-        fb[fn] = read_frag<QT, BN, BK>(tq, wn * C::kWTN + fn * 32, ks, lane);
+          for (int fm = 0; fm < C::kFM; ++fm)
+            fa[kr][fm] = read_frag<PT, BM, BK>(tp, wm * C::kWTM + fm * 32, kr, lane);
+#pragma unroll
+          for (int fn = 0; fn < C::kFN; ++fn)
+            fb[kr][fn] = read_frag<QT, BN, BK>(tq, wn * C::kWTN + fn * 32, kr, lane);
+        }
+        // keep the reads ahead of the multiplies (the scheduler would sink each to its use)
+        if constexpr (kHoist) __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
       for (int fm = 0; fm < C::kFM; ++fm)
 #pragma unroll
         for (int fn = 0; fn < C::kFN; ++fn) {
           if constexpr (SLAB > 0) {
-            slab[fm][fn] =
-                __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[fn], fa[fm], slab[fm][fn], 0, 0, 0);
+            slab[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][fn], fa[ks][fm],
+                                                                   slab[fm][fn], 0, 0, 0);
           } else {
-            acc[fm][fn] =
-                __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[fn], fa[fm], acc[fm][fn], 0, 0, 0);
+            acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][fn], fa[ks][fm],
+                                                                  acc[fm][fn], 0, 0, 0);
           }
         }
     }
