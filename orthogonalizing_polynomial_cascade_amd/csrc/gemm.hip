@@ -20,7 +20,10 @@
 //
 // The Gram and the polynomial are symmetric: only tiles on or above the diagonal are computed,
 // and each is stored twice (C[i][j] and C[j][i]) from the same fp32 value, so the stored matrices
-// are exactly symmetric.  Inside a diagonal tile only entries with i <= j are stored directly.
+// are exactly symmetric.  Inside a diagonal tile every entry is still stored once, in 16-byte
+// pieces of 8 columns: pieces on or above the diagonal and the 8x8 blocks the diagonal crosses
+// directly (an entry below the diagonal in such a block takes the value of its mirrored
+// position), pieces wholly below it by the mirror.
 //
 // Pipeline (CDNA4 / gfx950):
 //  * Operand slabs (rows x BK k, BK = 64 or 32) travel HBM -> LDS with buffer_load_dwordx4 ... lds
@@ -485,6 +488,35 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
     const int gi0 = i0 + wm * C::kWTM + fm * 32;   // first global row of this block
     const int gj0 = j0 + wn * C::kWTN;             // first global col of this wave
 
+    if constexpr (OP == OP_POLY) {
+      // B = b*A + c*(A*A): every piece of the block is combined in LDS first, so that the
+      // stores below (a diagonal tile's transposed reads and the mirror included) read
+      // finished values
+#pragma unroll
+      for (int pass = 0; pass < kPasses; ++pass) {
+        const int row = pass * kRowsPerPass + lane / kLanesPerRow;
+        const int col = (lane % kLanesPerRow) * 8;
+        if (gi0 + row >= p.M || gj0 + col >= p.N) continue;
+        const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(ep(row, col));
+        const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(ep(row, col + 4));
+        float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        const u32x4_t ae = ecur[pass];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float ba0 = p.alpha * bf16_to_f32(ae[e] & 0xFFFFu);
+          const float ba1 = p.alpha * bf16_to_f32(ae[e] >> 16);
+          const float cq0 = p.beta * v[2 * e];
+          const float cq1 = p.beta * v[2 * e + 1];
+          v[2 * e] = ba0 + cq0;
+          v[2 * e + 1] = ba1 + cq1;
+        }
+        *reinterpret_cast<f32x4_t*>(ep(row, col)) = f32x4_t{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<f32x4_t*>(ep(row, col + 4)) = f32x4_t{v[4], v[5], v[6], v[7]};
+      }
+      wait_lds();
+      __builtin_amdgcn_wave_barrier();
+    }
+
     // direct rows: each lane takes 8 consecutive columns of one row
 #pragma unroll
     for (int pass = 0; pass < kPasses; ++pass) {
@@ -515,38 +547,20 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
         }
         *reinterpret_cast<u32x4_t*>(Cb + (int64_t)gi * p.ldc + gj) = out;
       } else {
-        if constexpr (OP == OP_POLY) {
-          const u32x4_t ae = ecur[pass];
+        if (diag_tile && gj < gi) {
+          // below the diagonal of a diagonal tile: pieces wholly below are the mirror's; a piece
+          // that straddles it (gi - gj = d in 1..7) takes its entries e < d from the mirrored
+          // position (gj + e, gi), which this block holds d - e rows up and d columns right, so
+          // that the whole piece leaves as one 16-byte store
+          if (gi >= gj + 8) continue;
+          const int d = gi - gj;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float ba0 = p.alpha * bf16_to_f32(ae[e] & 0xFFFFu);
-            const float ba1 = p.alpha * bf16_to_f32(ae[e] >> 16);
-            const float cq0 = p.beta * v[2 * e];
-            const float cq1 = p.beta * v[2 * e + 1];
-            v[2 * e] = ba0 + cq0;
-            v[2 * e + 1] = ba1 + cq1;
-          }
-          // the mirror pass below reads the combined value back
-          *reinterpret_cast<f32x4_t*>(ep(row, col)) =
-              f32x4_t{v[0], v[1], v[2], v[3]};
-          *reinterpret_cast<f32x4_t*>(ep(row, col + 4)) =
-              f32x4_t{v[4], v[5], v[6], v[7]};
+          for (int e = 0; e < 7; ++e)
+            if (e < d) v[e] = *ep(row - d + e, col + d);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) out[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
-        if (!diag_tile || gi <= gj) {
-          *reinterpret_cast<u32x4_t*>(Cb + (int64_t)gi * p.ldc + gj) = out;
-        } else if (gi < gj + 8) {
-          // a diagonal tile's piece that straddles the diagonal: entries with gi <= gj + e only
-          // (the mirror pass writes the rest; pieces wholly below the diagonal are all its)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            if (gi <= gj + e) {
-              const uint32_t w = out[e >> 1];
-              Cb[(int64_t)gi * p.ldc + gj + e] = (uint16_t)((e & 1) ? (w >> 16) : (w & 0xFFFFu));
-            }
-          }
-        }
+        *reinterpret_cast<u32x4_t*>(Cb + (int64_t)gi * p.ldc + gj) = out;
         if (diag_tile) {
           if constexpr (OP == OP_GRAM) {
             if (gi >= gj && gi < gj + 8) {
@@ -571,17 +585,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
         const int gj = gj0 + col;
         const int gi = gi0 + rq * 8;
         if (gj >= p.N || gi >= p.M) continue;
-        if (diag_tile && gj < gi + 8) {
-          // entries with gi + e < gj only (gi + e == gj was stored directly)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            if (gi + e < gj) {
-              const float x = *ep(rq * 8 + e, col);
-              Cb[(int64_t)gj * p.ldc + gi + e] = (uint16_t)f32_to_bf16(x);
-            }
-          }
-          continue;
-        }
+        // a diagonal tile mirrors only pieces wholly below its diagonal (the direct pass wrote
+        // the pieces on and above it, and the 8x8 blocks the diagonal crosses)
+        if (diag_tile && gj < gi + 8) continue;
         float v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = *ep(rq * 8 + e, col);
