@@ -547,16 +547,24 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
         }
         *reinterpret_cast<u32x4_t*>(Cb + (int64_t)gi * p.ldc + gj) = out;
       } else {
-        if (diag_tile && gj < gi) {
+        if (diag_tile) {
           // below the diagonal of a diagonal tile: pieces wholly below are the mirror's; a piece
           // that straddles it (gi - gj = d in 1..7) takes its entries e < d from the mirrored
           // position (gj + e, gi), which this block holds d - e rows up and d columns right, so
-          // that the whole piece leaves as one 16-byte store
+          // that the whole piece leaves as one 16-byte store.  Every lane reads seven words (its
+          // own position where it needs none) so that the reads go out together.
           if (gi >= gj + 8) continue;
           const int d = gi - gj;
+          const bool straddle = d > 0;
+          const int tr = straddle ? row - d : row;
+          const int tc = straddle ? col + d : col;
+          const int tmax = straddle ? d - 1 : 0;
+          float t[7];
+#pragma unroll
+          for (int e = 0; e < 7; ++e) t[e] = *ep(tr + min(e, tmax), tc);
 #pragma unroll
           for (int e = 0; e < 7; ++e)
-            if (e < d) v[e] = *ep(row - d + e, col + d);
+            if (e < d) v[e] = t[e];
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) out[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
