@@ -299,6 +299,41 @@ def time_stages(anvil, w, reps=20):
     return res
 
 
+def time_library_products(w, reps=20):
+    """Context for the GEMM kernels: torch.bmm (hipBLASLt) on the same bf16 products with fp32
+    accumulation and bf16 output, but without the fused epilogues and computing the symmetric
+    products in full: the apply's X·B (tall) or B·X (wide), the Gram's full XᵀX or XXᵀ, and A·A.
+    Every operand is contiguous.  Microseconds per launch (HIP events around `reps` launches)."""
+    import torch
+    g, m, n = w.g, w.m, w.n
+    s = min(m, n)
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    x = torch.randn((g, m, n), generator=gen, device=dev).to(torch.bfloat16)
+    xt = x.transpose(1, 2).contiguous()
+    sq = torch.randn((g, s, s), generator=gen, device=dev).to(torch.bfloat16)
+    tall = m > n
+    prods = {
+        "apply_product": (x, sq) if tall else (sq, x),
+        "gram_full_product": (xt, x) if tall else (x, xt),
+        "poly_full_product": (sq, sq),
+    }
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, (p, q) in prods.items():
+        out = torch.bmm(p, q)
+        torch.cuda.synchronize()
+        e0, e1 = _events()
+        e0.record(stream)
+        for _ in range(reps):
+            torch.bmm(p, q, out=out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / reps * 1e3
+    return res
+
+
 # The six (a, b, c) maps of the cascade, as the library applies them (for the staged replay).
 ANVIL_MAPS = (
     (3.923798038567, -6.095026865488, 3.905234618423),
@@ -539,6 +574,10 @@ def main():
                      "algorithmic_bytes": 2 * w.g * (2 * w.m * w.n + min(w.m, w.n) ** 2),
                      "flops_per_launch": apply_flops},
     }
+    # the vendor library on the same products, for context (not part of the step)
+    lib = time_library_products(w)
+    line["library_bmm_us"] = dict(lib, note="torch.bmm (hipBLASLt), bf16 in and out, fp32 "
+                                  "accumulation, full products without the fused epilogues")
     # the rest of the bank update (equalizer and decay) on the same workload, timed after the
     # headline step; its tail is HBM-bound at 18 bytes per element (lane powers read the update,
     # the fused rescale-and-decay pass moves 16)
