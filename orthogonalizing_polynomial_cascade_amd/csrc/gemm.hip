@@ -280,7 +280,7 @@ struct Cfg {
       (STAGES * kStageBytes > kEpiBytes ? STAGES * kStageBytes : kEpiBytes);
   static_assert(kWTN % 8 == 0 && 64 % (kWTN / 8) == 0, "epilogue moves 8 columns per lane");
   static constexpr int kLoadsPerSlab = (BM + BN) * BK / 512 / kWaves;
-  static_assert(BK == 32 || BK == 64, "slab depth");
+  static_assert(BK == 32 || BK == 64 || BK == 128, "slab depth");
   static_assert(kWTM % 32 == 0 && kWTN % 32 == 0, "wave tile must be whole 32x32 fragments");
   static_assert(STAGES >= 2, "at least double buffering");
   static_assert(kLoadsPerSlab * (STAGES - 2) < 64, "vmcnt range");
@@ -684,11 +684,14 @@ constexpr int kSymTile = 128;
 // Small Grams and polynomials (at most 256 rows) take 32x32 tiles, one wave each: such launches
 // have few tiles (three per 256x768 matrix at 128x128) and each workgroup streams its operands at
 // a limited rate, so smaller tiles that spread the same work over more workgroups finish sooner.
+// Their slabs are 128 deep (32 KB of LDS): a slab iteration costs about the same whatever its
+// depth, and deeper slabs halve the iterations (256-deep ones cost the qk bank occupancy).
 // The Gram of a tall matrix reads X down its columns (K-major slabs of at least 128 rows) and
 // keeps 128x128.
 constexpr int kSmallSym = 256;
 int gram_tile(const Shape& sh) { return (!sh.tall() && sh.s() <= kSmallSym) ? 32 : kSymTile; }
 int poly_tile(int s) { return s <= kSmallSym ? 32 : kSymTile; }
+constexpr int kSmallBK = 128;
 // The Gram (K = the long side, up to thousands) sums each group of 8 slabs (512 k) in fresh
 // registers and adds the group sums to the running sums: on low-rank-dominated inputs one long
 // MFMA accumulation chain drifts from an fp64 reference noticeably more than fp32 sgemm does,
@@ -697,7 +700,7 @@ int poly_tile(int s) { return s <= kSmallSym ? 32 : kSymTile; }
 #ifndef ANVIL_SLAB_GROUP
 #define ANVIL_SLAB_GROUP 8
 #endif
-constexpr int kGramSlabGroup = ANVIL_SLAB_GROUP;
+constexpr int kGramSlabGroup = ANVIL_SLAB_GROUP;   // in 64-deep slabs: 512 k
 constexpr int kFullRound = 512;
 constexpr int kCus = 256;
 
@@ -724,7 +727,8 @@ hipError_t launch_gram(const uint16_t* x, uint16_t* a, float* trace_partials, co
   p.tiles_m = p.tiles_n = ceil_div(s, gram_tile(sh));
   p.tiles = p.tiles_m * (p.tiles_m + 1) / 2;
   if (gram_tile(sh) == 32)
-    return launch<OP_GRAM, false, false, 32, 32, 1, 1, 2, 64, kGramSlabGroup>(p, sh.g, stream);
+    return launch<OP_GRAM, false, false, 32, 32, 1, 1, 2, kSmallBK, kGramSlabGroup * 64 / kSmallBK>(
+        p, sh.g, stream);
   if (sh.tall())
     return launch<OP_GRAM, true, true, 128, 128, 2, 2, 2, 64, kGramSlabGroup>(p, sh.g, stream);
   return launch<OP_GRAM, false, false, 128, 128, 2, 2, 2, 64, kGramSlabGroup>(p, sh.g, stream);
@@ -750,7 +754,7 @@ hipError_t launch_poly(const uint16_t* a, uint16_t* bout, float coef_b, float co
   p.tiles_m = p.tiles_n = ceil_div(s, poly_tile(s));
   p.tiles = p.tiles_m * (p.tiles_m + 1) / 2;
   if (poly_tile(s) == 32)
-    return launch<OP_POLY, false, false, 32, 32, 1, 1, 2, 64, 0>(p, g, stream);
+    return launch<OP_POLY, false, false, 32, 32, 1, 1, 2, kSmallBK, 0>(p, g, stream);
   return launch<OP_POLY, false, false, 128, 128, 2, 4, 2, 64, 0>(p, g, stream);
 }
 
