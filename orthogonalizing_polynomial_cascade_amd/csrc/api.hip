@@ -161,15 +161,22 @@ int run_step(const MomentumIn& mi, float* velocity, uint16_t* out, const Shape& 
   if (e != hipSuccess) return hip_status(e);
   e = anvil::launch_normalize(X, A, partials, d, sh, stream);
   if (e != hipSuccess) return hip_status(e);
+  // small wide shapes (s <= 256, few matrices) form B inside the apply's launch
+  const bool fused = anvil::poly_apply_fused(sh);
   for (int k = 0; k < steps; ++k) {
     if (k > 0) {
       e = anvil::launch_gram(X, A, nullptr, sh, stream);
       if (e != hipSuccess) return hip_status(e);
     }
-    e = anvil::launch_poly(A, B, maps[k][1], maps[k][2], sh.g, sh.s(), stream);
-    if (e != hipSuccess) return hip_status(e);
-    e = anvil::launch_apply(X, B, Y, maps[k][0], split, sh, stream);
-    if (e != hipSuccess) return hip_status(e);
+    if (fused) {
+      e = anvil::launch_poly_apply(A, X, Y, maps[k][0], maps[k][1], maps[k][2], sh, stream);
+      if (e != hipSuccess) return hip_status(e);
+    } else {
+      e = anvil::launch_poly(A, B, maps[k][1], maps[k][2], sh.g, sh.s(), stream);
+      if (e != hipSuccess) return hip_status(e);
+      e = anvil::launch_apply(X, B, Y, maps[k][0], split, sh, stream);
+      if (e != hipSuccess) return hip_status(e);
+    }
     std::swap(X, Y);
   }
   return ANVIL_OK;

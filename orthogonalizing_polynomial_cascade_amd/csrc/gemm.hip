@@ -102,15 +102,17 @@ struct GemmParams {
 // ---------------------------------------------------------------------------------------------
 
 // [ROWS][BK] bf16: a row is BK*2 bytes = BK/8 slots of 16 bytes (8 k each), and 256 bytes of LDS
-// (one pass over the 64 banks) hold 16/(BK/8) rows.  Logical slot c of row r sits at slot
-// c ^ ((r / rows_per_256B) % slots): 16 consecutive rows read at one logical slot hit 16 distinct
-// 16-byte bank groups.
+// (one pass over the 64 banks) hold 16/(BK/8) rows, or one row spans BK/128 such passes.
+// Logical slot c of row r sits at slot c ^ ((r / rows_per_256B) % min(slots, 16)): 16
+// consecutive rows read at one logical slot hit 16 distinct 16-byte bank groups.
 template <int ROWS, int BK>
 struct KContig {
   static constexpr int kSlots = BK / 8;
-  static constexpr int kRowsPer256 = 16 / kSlots;
+  static constexpr int kRowsPer256 = kSlots >= 16 ? 1 : 16 / kSlots;
+  static constexpr int kSwizzle = kSlots >= 16 ? 16 : kSlots;
+  __device__ static __forceinline__ int swz(int row) { return (row / kRowsPer256) % kSwizzle; }
   __device__ static __forceinline__ int offset(int row, int c) {
-    return row * (BK * 2) + ((c ^ ((row / kRowsPer256) % kSlots)) << 4);
+    return row * (BK * 2) + ((c ^ swz(row)) << 4);
   }
 };
 
@@ -175,7 +177,7 @@ struct SlabCopy {
         constexpr int kSlots = BK / 8;
         constexpr int kRowsPerInst = 64 / kSlots;
         const int row = kRowsPerInst * u + lane / kSlots;
-        const int c = (lane % kSlots) ^ ((row / KContig<ROWS, BK>::kRowsPer256) % kSlots);
+        const int c = (lane % kSlots) ^ KContig<ROWS, BK>::swz(row);
         const int gr = row0 + row;
         kin[i] = c * 8;
         vbase[i] = gr < rows ? (uint32_t)(gr * ld + c * 8) * 2u : kOOB;
@@ -704,6 +706,231 @@ constexpr int kGramSlabGroup = ANVIL_SLAB_GROUP;   // in 64-deep slabs: 512 k
 constexpr int kFullRound = 512;
 constexpr int kCus = 256;
 
+
+// ---------------------------------------------------------------------------------------------
+// Fused polynomial and apply for small wide matrices (s = m <= 256 rows, m <= n): one launch per
+// map instead of two.  Each workgroup owns a 32 x 128 tile of C = a X + B X.  It first forms the
+// 32 rows of B = b A + c (A A) that the tile needs (all s columns; A is symmetric, so A A = A Aᵀ
+// with both operands read along their rows) in LDS, with the polynomial kernel's arithmetic for
+// every element: the same MFMA chain over k, the same epilogue expression and rounding (an entry
+// below the diagonal is the sum of the same products in the same order as its mirror, so it has
+// the same bits).  Then it multiplies those rows by the X slabs as the apply kernel does.  The
+// row block of B is formed once per column tile (n / 128 times), which costs little at these
+// sizes and saves the polynomial's launch.
+//
+// LDS: the 32 rows of A (later overwritten by the 32 rows of B) stay resident as one [32][256]
+// K-contiguous block, loaded once; the ring holds only the slabs of all rows of A (phase 1), then
+// the X slabs (phase 2); the accumulators are staged in the ring's space between the phases.
+// ---------------------------------------------------------------------------------------------
+
+struct PolyApplyParams {
+  const uint16_t* A;          // [g][s][s]
+  const uint16_t* X;          // [g][s][n]
+  uint16_t* C;                // [g][s][n]
+  int s, n;
+  float a, b, c;
+  int tiles_n;                // column tiles per matrix
+  int tiles;                  // tiles per matrix
+  int total;                  // tiles * g
+};
+
+constexpr int kPaRows = 32;         // tile rows (rows of B and of C)
+constexpr int kPaCols = 128;        // tile columns of C
+constexpr int kPaMaxS = 256;
+constexpr int kPaBK = 64;
+constexpr int kPaWaves = 4;
+constexpr int kPaBsBytes = kPaRows * kPaMaxS * 2;                       // 16 KB: A, then B, rows
+constexpr int kPaStage1 = kPaMaxS * kPaBK * 2;                          // 32 KB: all rows of A
+constexpr int kPaStage2 = kPaCols * kPaBK * 2;                          // 16 KB: X
+constexpr int kPaEpi1Pitch = kPaMaxS / kPaWaves + 4;                    // fp32 per staged row
+constexpr int kPaEpi2Pitch = kPaCols / kPaWaves + 4;
+constexpr int kPaEpi1Bytes = kPaWaves * kPaRows * kPaEpi1Pitch * 4;     // 34.8 KB
+constexpr int kPaRing2 = kPaBsBytes + kPaEpi1Bytes;                     // phase-2 ring offset
+constexpr int kPaLdsBytes =
+    kPaBsBytes + (2 * kPaStage1 > kPaEpi1Bytes + 2 * kPaStage2 ? 2 * kPaStage1
+                                                                : kPaEpi1Bytes + 2 * kPaStage2);
+static_assert(kPaRing2 % 16 == 0, "16-byte aligned phase-2 ring");
+static_assert(kPaBsBytes + kPaWaves * kPaRows * kPaEpi2Pitch * 4 <= kPaRing2,
+              "phase-2 staging below the phase-2 ring");
+
+__global__ __launch_bounds__(kPaWaves * 64) void poly_apply_kernel(PolyApplyParams p) {
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  const int logical = xcd_remap(blockIdx.x, p.total);
+  const int64_t b = logical / p.tiles;
+  const int t = logical % p.tiles;
+  const int i0 = (t / p.tiles_n) * kPaRows;
+  const int j0 = (t % p.tiles_n) * kPaCols;
+  const int s = p.s;
+
+  const uint16_t* Ab = p.A + b * (int64_t)s * s;
+  const uint16_t* Xb = p.X + b * (int64_t)s * p.n;
+  uint16_t* Cb = p.C + b * (int64_t)s * p.n;
+  const i32x4_t rA = make_rsrc(Ab, (uint32_t)((int64_t)s * s * 2));
+  const i32x4_t rX = make_rsrc(Xb, (uint32_t)((int64_t)s * p.n * 2));
+  char* Bs = smem;                 // [32][256] bf16, KContig<32, 256>: rows i0.. of A, then of B
+  using BsLayout = KContig<kPaRows, kPaMaxS>;
+  const uint32_t lds0 = lds_addr(smem);
+  const uint32_t ring1 = lds0 + kPaBsBytes;
+  const uint32_t ring2 = lds0 + kPaRing2;
+
+  // rows i0..i0+31 of A into Bs: instruction u (1 KB) holds rows 2u, 2u+1, lane L row 2u + L/32,
+  // physical slot L%32 = logical slot (L%32) ^ swizzle(row); zeros past s
+#pragma unroll
+  for (int q = 0; q < kPaRows / 2 / kPaWaves; ++q) {
+    const int u = wave + q * kPaWaves;
+    const int row = 2 * u + (lane >> 5);
+    const int c = (lane & 31) ^ BsLayout::swz(row);
+    const int gr = i0 + row;
+    const uint32_t voff = (gr < s && c * 8 < s) ? (uint32_t)(gr * s + c * 8) * 2u : kOOB;
+    dma16(rA, lds0 + (uint32_t)u * 1024u, voff);
+  }
+  // phase 1: the slabs of all rows of A (K-contiguous, 64 deep)
+  const SlabCopy<false, kPaMaxS, kPaBK, kPaWaves> copyQ1(s, 0, s, wave, lane);
+  constexpr int kFn1 = kPaMaxS / kPaWaves / 32;                      // 2 fragments per wave
+  const int KT = (s + kPaBK - 1) / kPaBK;
+  copyQ1.issue(rA, ring1, 0, s, wave);
+
+  // the X values of this wave's part of the final epilogue, fetched now (8 columns per lane)
+  constexpr int kLanesPerRow2 = (kPaCols / kPaWaves) / 8;   // 4
+  constexpr int kRowsPerPass2 = 64 / kLanesPerRow2;         // 16
+  constexpr int kPasses2 = kPaRows / kRowsPerPass2;         // 2
+  u32x4_t xe[kPasses2];
+#pragma unroll
+  for (int pass = 0; pass < kPasses2; ++pass) {
+    const int gi = i0 + pass * kRowsPerPass2 + lane / kLanesPerRow2;
+    const int gj = j0 + wave * (kPaCols / kPaWaves) + (lane % kLanesPerRow2) * 8;
+    xe[pass] = (gi < s && gj < p.n) ? *reinterpret_cast<const u32x4_t*>(Xb + (int64_t)gi * p.n + gj)
+                                    : u32x4_t{0u, 0u, 0u, 0u};
+  }
+
+  f32x16_t acc1[kFn1];
+#pragma unroll
+  for (int f = 0; f < kFn1; ++f)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc1[f][r] = 0.0f;
+  for (int kt = 0; kt < KT; ++kt) {
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (kt + 1 < KT)
+      copyQ1.issue(rA, ring1 + (uint32_t)(((kt + 1) & 1) * kPaStage1), (kt + 1) * kPaBK, s, wave);
+    const char* tq = smem + kPaBsBytes + (kt & 1) * kPaStage1;
+#pragma unroll
+    for (int ks = 0; ks < kPaBK / 16; ++ks) {
+      const bf16x8_t fa = read_frag<false, kPaRows, kPaMaxS>(Bs, 0, kt * (kPaBK / 16) + ks, lane);
+#pragma unroll
+      for (int f = 0; f < kFn1; ++f) {
+        const bf16x8_t fb =
+            read_frag<false, kPaMaxS, kPaBK>(tq, wave * (kPaMaxS / kPaWaves) + f * 32, ks, lane);
+        acc1[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb, fa, acc1[f], 0, 0, 0);
+      }
+    }
+  }
+  __syncthreads();   // the ring and the A rows are read: stage the accumulators, load X
+
+  const SlabCopy<true, kPaCols, kPaBK, kPaWaves> copyQ2(p.n, j0, p.n, wave, lane);
+  copyQ2.issue(rX, ring2, 0, s, wave);
+
+  // phase-1 epilogue: B = b*A + c*(A*A), rounded to bf16, in place of A in Bs (each lane reads
+  // the A piece it then overwrites; zeros past column s)
+  {
+    float* epi = reinterpret_cast<float*>(smem + kPaBsBytes) + wave * kPaRows * kPaEpi1Pitch;
+    auto ep = [&](int row, int col) { return epi + row * kPaEpi1Pitch + (col ^ (row & 16)); };
+#pragma unroll
+    for (int f = 0; f < kFn1; ++f)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int row = lane & 31;
+        const int col = f * 32 + 8 * q + 4 * (lane >> 5);
+        *reinterpret_cast<f32x4_t*>(ep(row, col)) =
+            f32x4_t{acc1[f][4 * q], acc1[f][4 * q + 1], acc1[f][4 * q + 2], acc1[f][4 * q + 3]};
+      }
+    wait_lds();
+    __builtin_amdgcn_wave_barrier();
+    constexpr int kLanesPerRow = (kPaMaxS / kPaWaves) / 8;   // 8
+    constexpr int kRowsPerPass = 64 / kLanesPerRow;           // 8
+#pragma unroll
+    for (int pass = 0; pass < kPaRows / kRowsPerPass; ++pass) {
+      const int row = pass * kRowsPerPass + lane / kLanesPerRow;
+      const int col = (lane % kLanesPerRow) * 8;
+      const int j = wave * (kPaMaxS / kPaWaves) + col;       // column of B (k of phase 2)
+      u32x4_t* piece = reinterpret_cast<u32x4_t*>(Bs + BsLayout::offset(row, j / 8));
+      const u32x4_t ae = *piece;
+      const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(ep(row, col));
+      const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(ep(row, col + 4));
+      const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      u32x4_t out = {0u, 0u, 0u, 0u};
+      if (j < s && i0 + row < s) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float ba0 = p.b * bf16_to_f32(ae[e] & 0xFFFFu);
+          const float ba1 = p.b * bf16_to_f32(ae[e] >> 16);
+          const float cq0 = p.c * v[2 * e];
+          const float cq1 = p.c * v[2 * e + 1];
+          out[e] = pack_bf16x2(ba0 + cq0, ba1 + cq1);
+        }
+      }
+      *piece = out;
+    }
+  }
+  __syncthreads();   // Bs holds B; the staging area is free
+
+  // ---- phase 2: C = a X + B X on columns j0.. (wave w: 32w .. 32w+31), K = s ----
+  f32x16_t acc2;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc2[r] = 0.0f;
+  for (int kt = 0; kt < KT; ++kt) {
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (kt + 1 < KT)
+      copyQ2.issue(rX, ring2 + (uint32_t)(((kt + 1) & 1) * kPaStage2), (kt + 1) * kPaBK, s, wave);
+    const char* tq = smem + kPaRing2 + (kt & 1) * kPaStage2;
+#pragma unroll
+    for (int ks = 0; ks < kPaBK / 16; ++ks) {
+      const bf16x8_t fa = read_frag<false, kPaRows, kPaMaxS>(Bs, 0, kt * (kPaBK / 16) + ks, lane);
+      const bf16x8_t fb = read_frag<true, kPaCols, kPaBK>(tq, wave * (kPaCols / kPaWaves), ks, lane);
+      acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb, fa, acc2, 0, 0, 0);
+    }
+  }
+
+  // phase-2 epilogue: C = bf16(a*X + B X), as the apply's fused form
+  {
+    float* epi = reinterpret_cast<float*>(smem + kPaBsBytes) + wave * kPaRows * kPaEpi2Pitch;
+    auto ep = [&](int row, int col) { return epi + row * kPaEpi2Pitch + (col ^ (row & 16)); };
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = lane & 31;
+      const int col = 8 * q + 4 * (lane >> 5);
+      *reinterpret_cast<f32x4_t*>(ep(row, col)) =
+          f32x4_t{acc2[4 * q], acc2[4 * q + 1], acc2[4 * q + 2], acc2[4 * q + 3]};
+    }
+    wait_lds();
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int pass = 0; pass < kPasses2; ++pass) {
+      const int row = pass * kRowsPerPass2 + lane / kLanesPerRow2;
+      const int col = (lane % kLanesPerRow2) * 8;
+      const int gi = i0 + row;
+      const int gj = j0 + wave * (kPaCols / kPaWaves) + col;
+      if (gi >= s || gj >= p.n) continue;
+      const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(ep(row, col));
+      const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(ep(row, col + 4));
+      const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      u32x4_t out;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float ax0 = p.a * bf16_to_f32(xe[pass][e] & 0xFFFFu);
+        const float ax1 = p.a * bf16_to_f32(xe[pass][e] >> 16);
+        out[e] = pack_bf16x2(ax0 + v[2 * e], ax1 + v[2 * e + 1]);
+      }
+      *reinterpret_cast<u32x4_t*>(Cb + (int64_t)gi * p.n + gj) = out;
+    }
+  }
+}
+
 }  // namespace
 
 int gram_trace_slots(const Shape& sh) { return ceil_div(sh.s(), gram_tile(sh)); }
@@ -804,15 +1031,66 @@ hipError_t launch_apply_cfg(const uint16_t* x, const uint16_t* bm, uint16_t* c, 
   return launch<OP_APPLY, false, true, BM, BN, WM, WN, STAGES, BK, 0>(p, sh.g, stream);
 }
 
+namespace {
+
+enum ApplyTiles { kApply128x256, kApply32x128, kApply128x128 };
+
+ApplyTiles apply_tiles(const Shape& sh) {
+  const int64_t wide_tiles = (int64_t)ceil_div(sh.m, 128) * ceil_div(sh.n, 256) * sh.g;
+  if (2 * wide_tiles >= kFullRound) return kApply128x256;
+  // launches with no more 128x128 tiles than CUs: 32x128 tiles, four times the workgroups
+  if ((int64_t)ceil_div(sh.m, 128) * ceil_div(sh.n, 128) * sh.g <= kCus) return kApply32x128;
+  return kApply128x128;
+}
+
+}  // namespace
+
 hipError_t launch_apply(const uint16_t* x, const uint16_t* bm, uint16_t* c, float coef_a,
                         bool split, const Shape& sh, hipStream_t stream) {
-  const int64_t wide_tiles = (int64_t)ceil_div(sh.m, 128) * ceil_div(sh.n, 256) * sh.g;
-  if (2 * wide_tiles >= kFullRound)
-    return launch_apply_cfg<128, 256, 2, 4, 2, 32>(x, bm, c, coef_a, split, sh, stream);
-  // launches with no more 128x128 tiles than CUs: 32x128 tiles, four times the workgroups
-  if ((int64_t)ceil_div(sh.m, 128) * ceil_div(sh.n, 128) * sh.g <= kCus)
-    return launch_apply_cfg<32, 128, 1, 2, 2, 64>(x, bm, c, coef_a, split, sh, stream);
-  return launch_apply_cfg<128, 128, 2, 4, 2, 64>(x, bm, c, coef_a, split, sh, stream);
+  switch (apply_tiles(sh)) {
+    case kApply128x256:
+      return launch_apply_cfg<128, 256, 2, 4, 2, 32>(x, bm, c, coef_a, split, sh, stream);
+    case kApply32x128:
+      return launch_apply_cfg<32, 128, 1, 2, 2, 64>(x, bm, c, coef_a, split, sh, stream);
+    default:
+      return launch_apply_cfg<128, 128, 2, 4, 2, 64>(x, bm, c, coef_a, split, sh, stream);
+  }
+}
+
+bool poly_apply_fused(const Shape& sh) {
+  return !sh.tall() && sh.s() <= kPaMaxS && sh.m <= 1024 && apply_tiles(sh) == kApply32x128;
+}
+
+hipError_t launch_poly_apply(const uint16_t* a, const uint16_t* x, uint16_t* c, float coef_a,
+                             float coef_b, float coef_c, const Shape& sh, hipStream_t stream) {
+  if (!poly_apply_fused(sh)) return hipErrorInvalidValue;
+  static std::atomic<uint64_t> configured{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (uint64_t(1) << dev) : 0;
+  if (bit == 0 || !(configured.load(std::memory_order_acquire) & bit)) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(poly_apply_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kPaLdsBytes);
+    if (e != hipSuccess) return e;
+    configured.fetch_or(bit, std::memory_order_release);
+  }
+  PolyApplyParams p{};
+  p.A = a;
+  p.X = x;
+  p.C = c;
+  p.s = sh.m;
+  p.n = sh.n;
+  p.a = coef_a;
+  p.b = coef_b;
+  p.c = coef_c;
+  p.tiles_n = ceil_div(sh.n, kPaCols);
+  p.tiles = ceil_div(sh.m, kPaRows) * p.tiles_n;
+  // g <= 256 here (the small-tile apply regime), so the grid fits one launch
+  p.total = (int)(p.tiles * sh.g);
+  hipLaunchKernelGGL(poly_apply_kernel, dim3((unsigned)p.total), dim3(kPaWaves * 64), kPaLdsBytes,
+                     stream, p);
+  return hipGetLastError();
 }
 
 }  // namespace anvil

@@ -37,6 +37,12 @@ hipError_t launch_poly(const uint16_t* a, uint16_t* b, float coef_b, float coef_
                        int s, hipStream_t stream);
 hipError_t launch_apply(const uint16_t* x, const uint16_t* b, uint16_t* c, float coef_a,
                         bool split, const Shape& sh, hipStream_t stream);
+// Polynomial and apply of one map in a single launch (C = a X + B X with B = b A + c A·A formed
+// per tile), for the wide shapes whose apply takes the small-tile configuration (s <= 256, few
+// matrices); the same arithmetic as launch_poly followed by launch_apply, element for element.
+bool poly_apply_fused(const Shape& sh);
+hipError_t launch_poly_apply(const uint16_t* a, const uint16_t* x, uint16_t* c, float coef_a,
+                             float coef_b, float coef_c, const Shape& sh, hipStream_t stream);
 
 // Equalizer lanes of an m x n matrix: rows when m >= n, else columns.
 int equalizer_lanes(const Shape& sh);

@@ -177,6 +177,21 @@ def test_deterministic_and_batch_invariant(gpu_lib, g, m, n):
         assert torch.equal(one.view(torch.int16), whole[i:i + 1].view(torch.int16))
 
 
+@pytest.mark.parametrize("g,m,n", [(24, 256, 768), (44, 200, 328), (66, 136, 136)])
+def test_fused_poly_apply_matches_stack(gpu_lib, g, m, n):
+    """Small wide matrices stepped alone form B inside the apply's launch (one launch per map
+    instead of two); in a stack this large the polynomial and the apply run as separate kernels
+    with 128x128 apply tiles.  Each matrix's step must be the same bit for bit either way."""
+    import torch
+    G = to_gpu_f32(_gauss_steps(g, m, n, 21, 1)[0])
+    vs = torch.randn((2, g, m, n), dtype=torch.float32, device="cuda")
+    whole = gpu_lib.anvil_bank_step(G, vs.clone(), 0.95, 0.85, 0.4385)
+    for i in (0, g // 2, g - 1):
+        one = gpu_lib.anvil_bank_step(G[i:i + 1].contiguous(), vs[:, i:i + 1].contiguous(), 0.95,
+                                      0.85, 0.4385)
+        assert torch.equal(one.view(torch.int16), whole[i:i + 1].view(torch.int16)), i
+
+
 def test_workspace_entry_and_streams_match(gpu_lib):
     import torch
     g, m, n = 2, 200, 328
