@@ -68,6 +68,23 @@ __global__ __launch_bounds__(256) void normalize_kernel(u32x4_t* __restrict__ x,
                                                         const float* __restrict__ partials,
                                                         int slots, float* __restrict__ d_out) {
   const int64_t b = blockIdx.y;
+  u32x4_t* xb = x + b * x_chunks;
+  u32x4_t* ab = a + b * a_chunks;
+  const int64_t total = x_chunks + a_chunks;
+  const int64_t chunk = (int64_t)kUnroll * blockDim.x;
+  const int64_t stride = chunk * gridDim.x;
+  auto load = [&](u32x4_t* v, int64_t base) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t i = base + (int64_t)u * blockDim.x;
+      if (i < total) v[u] = i < x_chunks ? xb[i] : ab[i - x_chunks];
+    }
+  };
+  // the first chunks are requested before the trace partials, so both latencies overlap
+  int64_t base = (int64_t)blockIdx.x * chunk + threadIdx.x;
+  u32x4_t v[kUnroll];
+  if (base < total) load(v, base);
+
   float tr = 0.0f;
   for (int s = 0; s < slots; ++s) tr += partials[b * slots + s];
   const float root = static_cast<float>(__builtin_sqrt(static_cast<double>(tr)));
@@ -79,18 +96,8 @@ __global__ __launch_bounds__(256) void normalize_kernel(u32x4_t* __restrict__ x,
   const Divisor dx{d, static_cast<float>(1.0 / static_cast<double>(d))};
   const Divisor da{dd, static_cast<float>(1.0 / static_cast<double>(dd))};
 
-  u32x4_t* xb = x + b * x_chunks;
-  u32x4_t* ab = a + b * a_chunks;
-  const int64_t total = x_chunks + a_chunks;
-  const int64_t chunk = (int64_t)kUnroll * blockDim.x;
-  const int64_t stride = chunk * gridDim.x;
-  for (int64_t base = (int64_t)blockIdx.x * chunk + threadIdx.x; base < total; base += stride) {
-    u32x4_t v[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t i = base + (int64_t)u * blockDim.x;
-      if (i < total) v[u] = i < x_chunks ? xb[i] : ab[i - x_chunks];
-    }
+  for (; base < total; base += stride) {
+    if (base != (int64_t)blockIdx.x * chunk + threadIdx.x) load(v, base);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t i = base + (int64_t)u * blockDim.x;
