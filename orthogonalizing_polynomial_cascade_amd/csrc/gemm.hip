@@ -318,6 +318,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
   const SlabCopy<PT, BM, BK, C::kWaves> copyP(p.ldp, i0, p.M, wave, lane);
   const SlabCopy<QT, BN, BK, C::kWaves> copyQ(p.ldq, j0, p.N, wave, lane);
   const uint32_t smem_lds = lds_addr(smem);
+  // A diagonal tile of a symmetric product has the same rows in both operands: it copies them once
+  // and reads both operands' fragments from that slab (with two stages every slab iteration waits
+  // for all of this wave's copies, so the copy count does not enter the waits).
+  const bool same_pq = STAGES == 2 && PT == QT && BM == BN && OP != OP_APPLY && ti == tj;
 
   f32x16_t acc[C::kFM][C::kFN];
 #pragma unroll
@@ -335,7 +339,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
     if (s < KT) {
       const uint32_t st = smem_lds + (uint32_t)(s * C::kStageBytes);
       copyP.issue(rP, st, s * BK, p.K, wave);
-      copyQ.issue(rQ, st + (uint32_t)C::kQOffset, s * BK, p.K, wave);
+      if (!same_pq) copyQ.issue(rQ, st + (uint32_t)C::kQOffset, s * BK, p.K, wave);
     }
   }
 
@@ -378,7 +382,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
       if (kn < KT) {
         const uint32_t st = smem_lds + (uint32_t)((kn % STAGES) * C::kStageBytes);
         copyP.issue(rP, st, kn * BK, p.K, wave);
-        copyQ.issue(rQ, st + (uint32_t)C::kQOffset, kn * BK, p.K, wave);
+        if (!same_pq) copyQ.issue(rQ, st + (uint32_t)C::kQOffset, kn * BK, p.K, wave);
       }
     }
     if constexpr (kHasE) {
@@ -386,7 +390,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
     }
     if (idle) continue;
     const char* tp = smem + (kt % STAGES) * C::kStageBytes;
-    const char* tq = tp + C::kQOffset;
+    const char* tq = same_pq ? tp : tp + C::kQOffset;
 
     // SLAB > 0: groups of SLAB consecutive slabs accumulate into fresh registers, which are then
     // added to the running sums (IEEE fp32 adds); SLAB == 0: the MFMAs accumulate into the
