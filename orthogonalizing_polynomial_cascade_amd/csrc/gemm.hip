@@ -23,14 +23,19 @@
 // are exactly symmetric.  Inside a diagonal tile every entry is still stored once, in 16-byte
 // pieces of 8 columns: pieces on or above the diagonal and the 8x8 blocks the diagonal crosses
 // directly (an entry below the diagonal in such a block takes the value of its mirrored
-// position), pieces wholly below it by the mirror.
+// position), pieces wholly below it by the mirror.  A diagonal tile has the same rows in both
+// operands: it copies them once, and its waves whose block lies wholly below the diagonal skip
+// their multiplies.
+//
+// For a few small wide matrices (s <= 256) poly_apply_kernel runs a map's polynomial and apply as
+// one launch, each workgroup forming the rows of B its tile needs (same bits as the two kernels).
 //
 // Pipeline (CDNA4 / gfx950):
-//  * Operand slabs (rows x BK k, BK = 64 or 32) travel HBM -> LDS with buffer_load_dwordx4 ... lds
-//    (16 bytes per lane straight into LDS, no register staging) through a ring of STAGES LDS
-//    buffers; the loads for slab k+STAGES-1 are in flight while slab k feeds the MFMAs.  Lanes
-//    outside the matrix (ragged M, N or K edges) get an offset past the buffer's range, which
-//    loads zeros.
+//  * Operand slabs (rows x BK k, BK = 32, 64 or 128) travel HBM -> LDS with
+//    buffer_load_dwordx4 ... lds (16 bytes per lane straight into LDS, no register staging)
+//    through a ring of STAGES LDS buffers; the loads for slab k+STAGES-1 are in flight while
+//    slab k feeds the MFMAs.  Lanes outside the matrix (ragged M, N or K edges) get an offset
+//    past the buffer's range, which loads zeros.
 //  * K-contiguous slabs are stored [row][BK k] with 16-byte slots XOR-swizzled by row, so that
 //    an MFMA operand (32 rows x 8 k) is one ds_read_b128 per lane without bank conflicts.
 //  * K-major slabs (X read down its columns, B by its rows k) are stored [BK k][rows] as they
@@ -895,7 +900,8 @@ __global__ __launch_bounds__(kPaWaves * 64) void poly_apply_kernel(PolyApplyPara
 #pragma unroll
     for (int ks = 0; ks < kPaBK / 16; ++ks) {
       const bf16x8_t fa = read_frag<false, kPaRows, kPaMaxS>(Bs, 0, kt * (kPaBK / 16) + ks, lane);
-      const bf16x8_t fb = read_frag<true, kPaCols, kPaBK>(tq, wave * (kPaCols / kPaWaves), ks, lane);
+      const bf16x8_t fb =
+          read_frag<true, kPaCols, kPaBK>(tq, wave * (kPaCols / kPaWaves), ks, lane);
       acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb, fa, acc2, 0, 0, 0);
     }
   }
