@@ -293,15 +293,25 @@ struct Cfg {
   static_assert(kLoadsPerSlab * (STAGES - 2) < 64, "vmcnt range");
 };
 
-template <int OP, bool PT, bool QT, int BM, int BN, int WM, int WN, int STAGES, int BK, int SLAB>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
+// KSPLIT > 1 (one-wave Gram tiles only): the tile's KSPLIT slab groups go to KSPLIT waves, each
+// with its own ring, which accumulate one group each from zero; the group sums are then added to
+// wave 0's in group order, which is exactly the one-wave kernel's running sum (0 + G0 = G0, then
+// + G1, + G2, ...), and wave 0 runs the epilogue.
+template <int OP, bool PT, bool QT, int BM, int BN, int WM, int WN, int STAGES, int BK, int SLAB,
+          int KSPLIT = 1>
+__global__ __launch_bounds__(WM * WN * KSPLIT * 64) void gemm_kernel(GemmParams p) {
   using C = Cfg<BM, BN, WM, WN, STAGES, BK>;
-  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  static_assert(KSPLIT == 1 || (OP == OP_GRAM && WM == 1 && WN == 1 && SLAB > 0 && STAGES == 2),
+                "k groups over waves: one-wave Gram tiles with slab groups and two stages");
+  extern __shared__ __attribute__((aligned(1024))) char smem_all[];
   __shared__ float sRed[C::kWaves];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = KSPLIT > 1 ? __builtin_amdgcn_readfirstlane(tid >> 6) : 0;   // k group
+  const bool computes = kg == 0;                                              // runs the epilogue
+  char* smem = smem_all + kg * C::kLdsBytes;                                  // this wave's ring
+  const int wave = KSPLIT > 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN;
   const int wn = wave % WN;
 
@@ -336,15 +346,17 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[fm][fn][r] = 0.0f;
 
-  const int KT = (p.K + BK - 1) / BK;
+  const int KT_all = (p.K + BK - 1) / BK;
+  const int kt0 = KSPLIT > 1 ? kg * SLAB : 0;                        // this wave's slabs
+  const int KT = KSPLIT > 1 ? min(KT_all, kt0 + SLAB) : KT_all;
 
-  // prologue: slabs 0 .. STAGES-2 in flight
+  // prologue: slabs kt0 .. kt0+STAGES-2 in flight (stage of slab kt: (kt - kt0) % STAGES)
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s) {
-    if (s < KT) {
+    if (kt0 + s < KT) {
       const uint32_t st = smem_lds + (uint32_t)(s * C::kStageBytes);
-      copyP.issue(rP, st, s * BK, p.K, wave);
-      if (!same_pq) copyQ.issue(rQ, st + (uint32_t)C::kQOffset, s * BK, p.K, wave);
+      copyP.issue(rP, st, (kt0 + s) * BK, p.K, wave);
+      if (!same_pq) copyQ.issue(rQ, st + (uint32_t)C::kQOffset, (kt0 + s) * BK, p.K, wave);
     }
   }
 
@@ -374,18 +386,24 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
   const bool idle = (OP != OP_APPLY) && ti == tj && wm * C::kWTM >= (wn + 1) * C::kWTN;
 
   f32x16_t slab[SLAB > 0 ? C::kFM : 1][SLAB > 0 ? C::kFN : 1];
-  for (int kt = 0; kt < KT; ++kt) {
+  for (int kt = kt0; kt < KT; ++kt) {
     // slab kt has landed once at most STAGES-2 younger slabs of this wave are still in flight
     if (KT - 1 - kt >= STAGES - 2) {
       wait_vmcnt<C::kLoadsPerSlab * (STAGES - 2)>();
     } else {
       wait_vmcnt<0>();
     }
-    __syncthreads();   // every wave's part of slab kt is in LDS; slab kt-1's buffer is free
+    // every wave's part of slab kt is in LDS; slab kt-1's buffer is free (a wave of a split tile
+    // reads only the slabs it copied itself)
+    if constexpr (KSPLIT == 1) {
+      __syncthreads();
+    } else {
+      __builtin_amdgcn_wave_barrier();
+    }
     {
       const int kn = kt + STAGES - 1;
       if (kn < KT) {
-        const uint32_t st = smem_lds + (uint32_t)((kn % STAGES) * C::kStageBytes);
+        const uint32_t st = smem_lds + (uint32_t)(((kn - kt0) % STAGES) * C::kStageBytes);
         copyP.issue(rP, st, kn * BK, p.K, wave);
         if (!same_pq) copyQ.issue(rQ, st + (uint32_t)C::kQOffset, kn * BK, p.K, wave);
       }
@@ -394,7 +412,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
       if (kt == KT - 1) load_e(ecur, 0);
     }
     if (idle) continue;
-    const char* tp = smem + (kt % STAGES) * C::kStageBytes;
+    const char* tp = smem + ((kt - kt0) % STAGES) * C::kStageBytes;
     const char* tq = same_pq ? tp : tp + C::kQOffset;
 
     // SLAB > 0: groups of SLAB consecutive slabs accumulate into fresh registers, which are then
@@ -459,6 +477,31 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
     }
   }
   __syncthreads();   // every wave is done with the operand ring; reuse it for the epilogue
+  if constexpr (KSPLIT > 1) {
+    // group sums of waves 1.. (in their own ring space) added to wave 0's in group order
+    if (!computes) {
+      float* red = reinterpret_cast<float*>(smem);
+#pragma unroll
+      for (int r = 0; r < 16; r += 4)
+        *reinterpret_cast<f32x4_t*>(red + lane * 16 + r) =
+            f32x4_t{acc[0][0][r], acc[0][0][r + 1], acc[0][0][r + 2], acc[0][0][r + 3]};
+    }
+    __syncthreads();
+    if (computes) {
+#pragma unroll
+      for (int w = 1; w < KSPLIT; ++w) {
+        const float* red = reinterpret_cast<const float*>(smem_all + w * C::kLdsBytes);
+#pragma unroll
+        for (int r = 0; r < 16; r += 4) {
+          const f32x4_t v = *reinterpret_cast<const f32x4_t*>(red + lane * 16 + r);
+          acc[0][0][r] += v[0];
+          acc[0][0][r + 1] += v[1];
+          acc[0][0][r + 2] += v[2];
+          acc[0][0][r + 3] += v[3];
+        }
+      }
+    }
+  }
 
   // ---------------- epilogue: per wave, 32 rows at a time through LDS ----------------
   // With the MFMA operands as (Q, P) the fragment holds C transposed: register r of lane l is
@@ -479,6 +522,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
 
 #pragma unroll
   for (int fm = 0; fm < C::kFM; ++fm) {
+    if (!computes) break;
     u32x4_t enext[kHasE ? kPasses : 1];
     if constexpr (kHasE) {
       if (fm + 1 < C::kFM) load_e(enext, fm + 1);
@@ -631,7 +675,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
       // fixed-order reduction: butterfly within each wave, then waves in index order
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) tsum += __shfl_xor(tsum, off, 64);
-      if (lane == 0) sRed[wave] = tsum;
+      if (lane == 0 && computes) sRed[wave] = tsum;
       __syncthreads();
       if (tid == 0) {
         float s = 0.0f;
@@ -644,10 +688,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-template <int OP, bool PT, bool QT, int BM, int BN, int WM, int WN, int STAGES, int BK, int SLAB>
+template <int OP, bool PT, bool QT, int BM, int BN, int WM, int WN, int STAGES, int BK, int SLAB,
+          int KSPLIT = 1>
 hipError_t launch(GemmParams p, int64_t g, hipStream_t stream) {
   using C = Cfg<BM, BN, WM, WN, STAGES, BK>;
-  auto kern = gemm_kernel<OP, PT, QT, BM, BN, WM, WN, STAGES, BK, SLAB>;
+  auto kern = gemm_kernel<OP, PT, QT, BM, BN, WM, WN, STAGES, BK, SLAB, KSPLIT>;
+  constexpr int kThreads = C::kThreads * KSPLIT;
+  constexpr int kLdsBytes = C::kLdsBytes * KSPLIT;
   // raise the dynamic LDS limit once per instantiation and device (bit d of the mask: device d;
   // devices past 63 set it on every launch)
   static std::atomic<uint64_t> configured{0};
@@ -657,14 +704,14 @@ hipError_t launch(GemmParams p, int64_t g, hipStream_t stream) {
   const uint64_t bit = dev < 64 ? (uint64_t(1) << dev) : 0;
   if (bit == 0 || !(configured.load(std::memory_order_acquire) & bit)) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (e != hipSuccess) return e;
     configured.fetch_or(bit, std::memory_order_release);
   }
   // A dispatch counts its work-items in 32 bits: a stack whose tiles need more goes out as
   // consecutive sub-stacks (every matrix keeps its own tiles, so nothing in its arithmetic moves).
   const int64_t per_launch =
-      std::max<int64_t>(1, int64_t(UINT32_MAX) / ((int64_t)p.tiles * C::kThreads));
+      std::max<int64_t>(1, int64_t(UINT32_MAX) / ((int64_t)p.tiles * kThreads));
   for (int64_t b0 = 0; b0 < g; b0 += per_launch) {
     const int64_t gb = std::min(per_launch, g - b0);
     GemmParams q = p;
@@ -674,7 +721,7 @@ hipError_t launch(GemmParams p, int64_t g, hipStream_t stream) {
     if (q.E) q.E += b0 * p.strideE;
     if (q.trace) q.trace += b0 * p.trace_slots;
     q.total = (int)(p.tiles * gb);
-    hipLaunchKernelGGL(kern, dim3((unsigned)q.total), dim3(C::kThreads), C::kLdsBytes, stream, q);
+    hipLaunchKernelGGL(kern, dim3((unsigned)q.total), dim3(kThreads), kLdsBytes, stream, q);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -703,6 +750,9 @@ constexpr int kSmallSym = 256;
 int gram_tile(const Shape& sh) { return (!sh.tall() && sh.s() <= kSmallSym) ? 32 : kSymTile; }
 int poly_tile(int s) { return s <= kSmallSym ? 32 : kSymTile; }
 constexpr int kSmallBK = 128;
+// The small Gram (k up to a few thousand) sums groups of 256 k, which its k-split launch spreads
+// over waves; the larger Grams sum groups of 512 k (kGramSlabGroup).
+constexpr int kSmallGroupK = 256;
 // The Gram (K = the long side, up to thousands) sums each group of 8 slabs (512 k) in fresh
 // registers and adds the group sums to the running sums: on low-rank-dominated inputs one long
 // MFMA accumulation chain drifts from an fp64 reference noticeably more than fp32 sgemm does,
@@ -963,9 +1013,21 @@ hipError_t launch_gram(const uint16_t* x, uint16_t* a, float* trace_partials, co
   p.trace_slots = gram_trace_slots(sh);
   p.tiles_m = p.tiles_n = ceil_div(s, gram_tile(sh));
   p.tiles = p.tiles_m * (p.tiles_m + 1) / 2;
-  if (gram_tile(sh) == 32)
-    return launch<OP_GRAM, false, false, 32, 32, 1, 1, 2, kSmallBK, kGramSlabGroup * 64 / kSmallBK>(
-        p, sh.g, stream);
+  if (gram_tile(sh) == 32) {
+    // A launch whose one-wave tiles fit one round on the CUs gives each 256-k group of a tile to
+    // a wave of its own (KSPLIT); the sums and their order are those of the one-wave tile.
+    constexpr int kSlab = kSmallGroupK / kSmallBK;
+    const int groups = ceil_div(ceil_div(p.K, kSmallBK), kSlab);
+    if ((int64_t)p.tiles * sh.g <= kCus) {
+      if (groups == 2)
+        return launch<OP_GRAM, false, false, 32, 32, 1, 1, 2, kSmallBK, kSlab, 2>(p, sh.g, stream);
+      if (groups == 3)
+        return launch<OP_GRAM, false, false, 32, 32, 1, 1, 2, kSmallBK, kSlab, 3>(p, sh.g, stream);
+      if (groups == 4)
+        return launch<OP_GRAM, false, false, 32, 32, 1, 1, 2, kSmallBK, kSlab, 4>(p, sh.g, stream);
+    }
+    return launch<OP_GRAM, false, false, 32, 32, 1, 1, 2, kSmallBK, kSlab>(p, sh.g, stream);
+  }
   if (sh.tall())
     return launch<OP_GRAM, true, true, 128, 128, 2, 2, 2, 64, kGramSlabGroup>(p, sh.g, stream);
   return launch<OP_GRAM, false, false, 128, 128, 2, 2, 2, 64, kGramSlabGroup>(p, sh.g, stream);
