@@ -173,6 +173,7 @@ struct SlabCopy {
   int kin[kInsts];          // the lane's k offset inside the slab (for the ragged last slab)
   uint32_t kbytes;          // bytes per unit of k0
 
+  SlabCopy() = default;
   __device__ __forceinline__ SlabCopy(int ld, int row0, int rows, int wave, int lane) {
     kbytes = KMAJOR ? 2u * (uint32_t)ld : 2u;
 #pragma unroll
@@ -293,25 +294,31 @@ struct Cfg {
   static_assert(kLoadsPerSlab * (STAGES - 2) < 64, "vmcnt range");
 };
 
-// KSPLIT > 1 (one-wave Gram tiles only): the tile's KSPLIT slab groups go to KSPLIT waves, each
-// with its own ring, which accumulate one group each from zero; the group sums are then added to
-// wave 0's in group order, which is exactly the one-wave kernel's running sum (0 + G0 = G0, then
-// + G1, + G2, ...), and wave 0 runs the epilogue.
+// KSPLIT > 1 (Gram tiles with slab groups only): the tile's KSPLIT slab groups go to KSPLIT sets
+// of WM x WN waves, each set with its own ring, which accumulate one group each from zero; the
+// group sums are then added to the first set's in group order, which is exactly the unsplit
+// kernel's running sum (0 + G0 = G0, then + G1, + G2, ...), and the first set runs the epilogue.
+// With several waves per set every wave runs SLAB iterations (skipping slabs past its k range),
+// so that all waves meet every barrier; such a tile writes one trace partial per 32-row diagonal
+// wave block, the partials of 32x32 tiles.
 template <int OP, bool PT, bool QT, int BM, int BN, int WM, int WN, int STAGES, int BK, int SLAB,
           int KSPLIT = 1>
 __global__ __launch_bounds__(WM * WN * KSPLIT * 64) void gemm_kernel(GemmParams p) {
   using C = Cfg<BM, BN, WM, WN, STAGES, BK>;
-  static_assert(KSPLIT == 1 || (OP == OP_GRAM && WM == 1 && WN == 1 && SLAB > 0 && STAGES == 2),
-                "k groups over waves: one-wave Gram tiles with slab groups and two stages");
+  static_assert(KSPLIT == 1 || (OP == OP_GRAM && SLAB > 0 && STAGES == 2),
+                "k groups over waves: Gram tiles with slab groups and two stages");
+  static_assert(KSPLIT == 1 || C::kWaves == 1 || (WM == WN && C::kWTM == 32 && C::kWTN == 32),
+                "a split tile of several waves has 32x32 wave blocks on its diagonal");
   extern __shared__ __attribute__((aligned(1024))) char smem_all[];
   __shared__ float sRed[C::kWaves];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int kg = KSPLIT > 1 ? __builtin_amdgcn_readfirstlane(tid >> 6) : 0;   // k group
-  const bool computes = kg == 0;                                              // runs the epilogue
-  char* smem = smem_all + kg * C::kLdsBytes;                                  // this wave's ring
-  const int wave = KSPLIT > 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = KSPLIT > 1 ? wave_all / C::kWaves : 0;                     // k group
+  const bool computes = kg == 0;                                           // runs the epilogue
+  char* smem = smem_all + kg * C::kLdsBytes;                               // this group's ring
+  const int wave = KSPLIT > 1 ? wave_all % C::kWaves : wave_all;
   const int wm = wave / WN;
   const int wn = wave % WN;
 
@@ -386,7 +393,9 @@ __global__ __launch_bounds__(WM * WN * KSPLIT * 64) void gemm_kernel(GemmParams 
   const bool idle = (OP != OP_APPLY) && ti == tj && wm * C::kWTM >= (wn + 1) * C::kWTN;
 
   f32x16_t slab[SLAB > 0 ? C::kFM : 1][SLAB > 0 ? C::kFN : 1];
-  for (int kt = kt0; kt < KT; ++kt) {
+  constexpr bool kPadded = KSPLIT > 1 && C::kWaves > 1;   // uniform trip count: shared barriers
+  const int kt_last = kPadded ? kt0 + SLAB : KT;
+  for (int kt = kt0; kt < kt_last; ++kt) {
     // slab kt has landed once at most STAGES-2 younger slabs of this wave are still in flight
     if (KT - 1 - kt >= STAGES - 2) {
       wait_vmcnt<C::kLoadsPerSlab * (STAGES - 2)>();
@@ -395,7 +404,7 @@ __global__ __launch_bounds__(WM * WN * KSPLIT * 64) void gemm_kernel(GemmParams 
     }
     // every wave's part of slab kt is in LDS; slab kt-1's buffer is free (a wave of a split tile
     // reads only the slabs it copied itself)
-    if constexpr (KSPLIT == 1) {
+    if constexpr (KSPLIT == 1 || C::kWaves > 1) {
       __syncthreads();
     } else {
       __builtin_amdgcn_wave_barrier();
@@ -408,6 +417,7 @@ __global__ __launch_bounds__(WM * WN * KSPLIT * 64) void gemm_kernel(GemmParams 
         if (!same_pq) copyQ.issue(rQ, st + (uint32_t)C::kQOffset, kn * BK, p.K, wave);
       }
     }
+    if (kPadded && kt >= KT) continue;
     if constexpr (kHasE) {
       if (kt == KT - 1) load_e(ecur, 0);
     }
@@ -478,27 +488,40 @@ __global__ __launch_bounds__(WM * WN * KSPLIT * 64) void gemm_kernel(GemmParams 
   }
   __syncthreads();   // every wave is done with the operand ring; reuse it for the epilogue
   if constexpr (KSPLIT > 1) {
-    // group sums of waves 1.. (in their own ring space) added to wave 0's in group order
+    // group sums of the later sets (in their own ring space, per wave and lane) added to the
+    // first set's in group order
+    constexpr int kFrags = C::kFM * C::kFN;
+    static_assert(C::kWaves * kFrags * 16 * 64 * 4 <= C::kLdsBytes, "group sums fit the ring");
     if (!computes) {
-      float* red = reinterpret_cast<float*>(smem);
+      float* red = reinterpret_cast<float*>(smem) + (wave * 64 + lane) * kFrags * 16;
 #pragma unroll
-      for (int r = 0; r < 16; r += 4)
-        *reinterpret_cast<f32x4_t*>(red + lane * 16 + r) =
-            f32x4_t{acc[0][0][r], acc[0][0][r + 1], acc[0][0][r + 2], acc[0][0][r + 3]};
+      for (int fm = 0; fm < C::kFM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < C::kFN; ++fn)
+#pragma unroll
+          for (int r = 0; r < 16; r += 4)
+            *reinterpret_cast<f32x4_t*>(red + (fm * C::kFN + fn) * 16 + r) =
+                f32x4_t{acc[fm][fn][r], acc[fm][fn][r + 1], acc[fm][fn][r + 2], acc[fm][fn][r + 3]};
     }
     __syncthreads();
     if (computes) {
 #pragma unroll
       for (int w = 1; w < KSPLIT; ++w) {
-        const float* red = reinterpret_cast<const float*>(smem_all + w * C::kLdsBytes);
+        const float* red = reinterpret_cast<const float*>(smem_all + w * C::kLdsBytes) +
+                           (wave * 64 + lane) * kFrags * 16;
 #pragma unroll
-        for (int r = 0; r < 16; r += 4) {
-          const f32x4_t v = *reinterpret_cast<const f32x4_t*>(red + lane * 16 + r);
-          acc[0][0][r] += v[0];
-          acc[0][0][r + 1] += v[1];
-          acc[0][0][r + 2] += v[2];
-          acc[0][0][r + 3] += v[3];
-        }
+        for (int fm = 0; fm < C::kFM; ++fm)
+#pragma unroll
+          for (int fn = 0; fn < C::kFN; ++fn)
+#pragma unroll
+            for (int r = 0; r < 16; r += 4) {
+              const f32x4_t v =
+                  *reinterpret_cast<const f32x4_t*>(red + (fm * C::kFN + fn) * 16 + r);
+              acc[fm][fn][r] += v[0];
+              acc[fm][fn][r + 1] += v[1];
+              acc[fm][fn][r + 2] += v[2];
+              acc[fm][fn][r + 3] += v[3];
+            }
       }
     }
   }
@@ -675,12 +698,18 @@ __global__ __launch_bounds__(WM * WN * KSPLIT * 64) void gemm_kernel(GemmParams 
       // fixed-order reduction: butterfly within each wave, then waves in index order
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) tsum += __shfl_xor(tsum, off, 64);
-      if (lane == 0 && computes) sRed[wave] = tsum;
-      __syncthreads();
-      if (tid == 0) {
-        float s = 0.0f;
-        for (int w = 0; w < C::kWaves; ++w) s += sRed[w];
-        p.trace[b * p.trace_slots + ti] = s;
+      if constexpr (KSPLIT > 1 && C::kWaves > 1) {
+        // one partial per diagonal 32x32 wave block, as a 32x32 tile writes it
+        if (lane == 0 && computes && wm == wn && i0 + wm * 32 < p.M)
+          p.trace[b * p.trace_slots + ti * WM + wm] = tsum;
+      } else {
+        if (lane == 0 && computes) sRed[wave] = tsum;
+        __syncthreads();
+        if (tid == 0) {
+          float s = 0.0f;
+          for (int w = 0; w < C::kWaves; ++w) s += sRed[w];
+          p.trace[b * p.trace_slots + ti] = s;
+        }
       }
     }
   }
@@ -794,25 +823,38 @@ struct PolyApplyParams {
 };
 
 constexpr int kPaRows = 32;         // tile rows (rows of B and of C)
-constexpr int kPaCols = 128;        // tile columns of C
+constexpr int kPaChunk = 128;       // columns of C per chunk; a tile is NC chunks
 constexpr int kPaMaxS = 256;
 constexpr int kPaBK = 64;
 constexpr int kPaWaves = 4;
 constexpr int kPaBsBytes = kPaRows * kPaMaxS * 2;                       // 16 KB: A, then B, rows
 constexpr int kPaStage1 = kPaMaxS * kPaBK * 2;                          // 32 KB: all rows of A
-constexpr int kPaStage2 = kPaCols * kPaBK * 2;                          // 16 KB: X
 constexpr int kPaEpi1Pitch = kPaMaxS / kPaWaves + 4;                    // fp32 per staged row
-constexpr int kPaEpi2Pitch = kPaCols / kPaWaves + 4;
+constexpr int kPaEpi2Pitch = kPaChunk / kPaWaves + 4;
 constexpr int kPaEpi1Bytes = kPaWaves * kPaRows * kPaEpi1Pitch * 4;     // 34.8 KB
 constexpr int kPaRing2 = kPaBsBytes + kPaEpi1Bytes;                     // phase-2 ring offset
-constexpr int kPaLdsBytes =
-    kPaBsBytes + (2 * kPaStage1 > kPaEpi1Bytes + 2 * kPaStage2 ? 2 * kPaStage1
-                                                                : kPaEpi1Bytes + 2 * kPaStage2);
 static_assert(kPaRing2 % 16 == 0, "16-byte aligned phase-2 ring");
 static_assert(kPaBsBytes + kPaWaves * kPaRows * kPaEpi2Pitch * 4 <= kPaRing2,
               "phase-2 staging below the phase-2 ring");
 
+// A tile of NC chunks of 128 columns: wave w owns columns 32w..32w+31 of every chunk.  The X
+// slabs of the chunks sit side by side in a stage (64 deep, or 32 deep for more than three
+// chunks, so that two stages fit beside the rows of B and the phase-1 staging).
+template <int NC>
+struct PaCfg {
+  static constexpr int kCols = kPaChunk * NC;
+  static constexpr int kBK2 = NC <= 3 ? 64 : 32;
+  static constexpr int kChunkBytes = kPaChunk * kBK2 * 2;
+  static constexpr int kStage2 = NC * kChunkBytes;
+  static constexpr int kLdsBytes =
+      kPaBsBytes + (2 * kPaStage1 > kPaEpi1Bytes + 2 * kStage2 ? 2 * kPaStage1
+                                                               : kPaEpi1Bytes + 2 * kStage2);
+  static_assert(kLdsBytes <= 160 * 1024, "LDS of one CU");
+};
+
+template <int NC>
 __global__ __launch_bounds__(kPaWaves * 64) void poly_apply_kernel(PolyApplyParams p) {
+  using PC = PaCfg<NC>;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -822,7 +864,7 @@ __global__ __launch_bounds__(kPaWaves * 64) void poly_apply_kernel(PolyApplyPara
   const int64_t b = logical / p.tiles;
   const int t = logical % p.tiles;
   const int i0 = (t / p.tiles_n) * kPaRows;
-  const int j0 = (t % p.tiles_n) * kPaCols;
+  const int j0 = (t % p.tiles_n) * PC::kCols;
   const int s = p.s;
 
   const uint16_t* Ab = p.A + b * (int64_t)s * s;
@@ -854,17 +896,21 @@ __global__ __launch_bounds__(kPaWaves * 64) void poly_apply_kernel(PolyApplyPara
   copyQ1.issue(rA, ring1, 0, s, wave);
 
   // the X values of this wave's part of the final epilogue, fetched now (8 columns per lane)
-  constexpr int kLanesPerRow2 = (kPaCols / kPaWaves) / 8;   // 4
+  constexpr int kLanesPerRow2 = (kPaChunk / kPaWaves) / 8;  // 4
   constexpr int kRowsPerPass2 = 64 / kLanesPerRow2;         // 16
   constexpr int kPasses2 = kPaRows / kRowsPerPass2;         // 2
-  u32x4_t xe[kPasses2];
+  u32x4_t xe[NC][kPasses2];
 #pragma unroll
-  for (int pass = 0; pass < kPasses2; ++pass) {
-    const int gi = i0 + pass * kRowsPerPass2 + lane / kLanesPerRow2;
-    const int gj = j0 + wave * (kPaCols / kPaWaves) + (lane % kLanesPerRow2) * 8;
-    xe[pass] = (gi < s && gj < p.n) ? *reinterpret_cast<const u32x4_t*>(Xb + (int64_t)gi * p.n + gj)
-                                    : u32x4_t{0u, 0u, 0u, 0u};
-  }
+  for (int ch = 0; ch < NC; ++ch)
+#pragma unroll
+    for (int pass = 0; pass < kPasses2; ++pass) {
+      const int gi = i0 + pass * kRowsPerPass2 + lane / kLanesPerRow2;
+      const int gj =
+          j0 + ch * kPaChunk + wave * (kPaChunk / kPaWaves) + (lane % kLanesPerRow2) * 8;
+      xe[ch][pass] = (gi < s && gj < p.n)
+                         ? *reinterpret_cast<const u32x4_t*>(Xb + (int64_t)gi * p.n + gj)
+                         : u32x4_t{0u, 0u, 0u, 0u};
+    }
 
   f32x16_t acc1[kFn1];
 #pragma unroll
@@ -890,8 +936,17 @@ __global__ __launch_bounds__(kPaWaves * 64) void poly_apply_kernel(PolyApplyPara
   }
   __syncthreads();   // the ring and the A rows are read: stage the accumulators, load X
 
-  const SlabCopy<true, kPaCols, kPaBK, kPaWaves> copyQ2(p.n, j0, p.n, wave, lane);
-  copyQ2.issue(rX, ring2, 0, s, wave);
+  // the X slabs of the chunks (chunk ch at ch * kChunkBytes of a stage)
+  using Copy2 = SlabCopy<true, kPaChunk, PC::kBK2, kPaWaves>;
+  Copy2 copyQ2[NC];
+#pragma unroll
+  for (int ch = 0; ch < NC; ++ch) copyQ2[ch] = Copy2(p.n, j0 + ch * kPaChunk, p.n, wave, lane);
+  auto issue2 = [&](uint32_t dst, int k0) {
+#pragma unroll
+    for (int ch = 0; ch < NC; ++ch)
+      copyQ2[ch].issue(rX, dst + (uint32_t)(ch * PC::kChunkBytes), k0, s, wave);
+  };
+  issue2(ring2, 0);
 
   // phase-1 epilogue: B = b*A + c*(A*A), rounded to bf16, in place of A in Bs (each lane reads
   // the A piece it then overwrites; zeros past column s)
@@ -937,35 +992,42 @@ __global__ __launch_bounds__(kPaWaves * 64) void poly_apply_kernel(PolyApplyPara
   }
   __syncthreads();   // Bs holds B; the staging area is free
 
-  // ---- phase 2: C = a X + B X on columns j0.. (wave w: 32w .. 32w+31), K = s ----
-  f32x16_t acc2;
+  // ---- phase 2: C = a X + B X on the chunks' columns (wave w: 32w .. 32w+31 of each), K = s ----
+  constexpr int kKs2 = PC::kBK2 / 16;
+  const int KT2 = (s + PC::kBK2 - 1) / PC::kBK2;
+  f32x16_t acc2[NC];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc2[r] = 0.0f;
-  for (int kt = 0; kt < KT; ++kt) {
+  for (int ch = 0; ch < NC; ++ch)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc2[ch][r] = 0.0f;
+  for (int kt = 0; kt < KT2; ++kt) {
     wait_vmcnt<0>();
     __syncthreads();
-    if (kt + 1 < KT)
-      copyQ2.issue(rX, ring2 + (uint32_t)(((kt + 1) & 1) * kPaStage2), (kt + 1) * kPaBK, s, wave);
-    const char* tq = smem + kPaRing2 + (kt & 1) * kPaStage2;
+    if (kt + 1 < KT2) issue2(ring2 + (uint32_t)(((kt + 1) & 1) * PC::kStage2), (kt + 1) * PC::kBK2);
+    const char* tq = smem + kPaRing2 + (kt & 1) * PC::kStage2;
 #pragma unroll
-    for (int ks = 0; ks < kPaBK / 16; ++ks) {
-      const bf16x8_t fa = read_frag<false, kPaRows, kPaMaxS>(Bs, 0, kt * (kPaBK / 16) + ks, lane);
-      const bf16x8_t fb =
-          read_frag<true, kPaCols, kPaBK>(tq, wave * (kPaCols / kPaWaves), ks, lane);
-      acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb, fa, acc2, 0, 0, 0);
+    for (int ks = 0; ks < kKs2; ++ks) {
+      const bf16x8_t fa = read_frag<false, kPaRows, kPaMaxS>(Bs, 0, kt * kKs2 + ks, lane);
+#pragma unroll
+      for (int ch = 0; ch < NC; ++ch) {
+        const bf16x8_t fb = read_frag<true, kPaChunk, PC::kBK2>(
+            tq + ch * PC::kChunkBytes, wave * (kPaChunk / kPaWaves), ks, lane);
+        acc2[ch] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb, fa, acc2[ch], 0, 0, 0);
+      }
     }
   }
 
-  // phase-2 epilogue: C = bf16(a*X + B X), as the apply's fused form
-  {
-    float* epi = reinterpret_cast<float*>(smem + kPaBsBytes) + wave * kPaRows * kPaEpi2Pitch;
-    auto ep = [&](int row, int col) { return epi + row * kPaEpi2Pitch + (col ^ (row & 16)); };
+  // phase-2 epilogue: C = bf16(a*X + B X), as the apply's fused form, one chunk at a time
+  float* epi = reinterpret_cast<float*>(smem + kPaBsBytes) + wave * kPaRows * kPaEpi2Pitch;
+  auto ep = [&](int row, int col) { return epi + row * kPaEpi2Pitch + (col ^ (row & 16)); };
+#pragma unroll
+  for (int ch = 0; ch < NC; ++ch) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int row = lane & 31;
       const int col = 8 * q + 4 * (lane >> 5);
       *reinterpret_cast<f32x4_t*>(ep(row, col)) =
-          f32x4_t{acc2[4 * q], acc2[4 * q + 1], acc2[4 * q + 2], acc2[4 * q + 3]};
+          f32x4_t{acc2[ch][4 * q], acc2[ch][4 * q + 1], acc2[ch][4 * q + 2], acc2[ch][4 * q + 3]};
     }
     wait_lds();
     __builtin_amdgcn_wave_barrier();
@@ -974,7 +1036,7 @@ __global__ __launch_bounds__(kPaWaves * 64) void poly_apply_kernel(PolyApplyPara
       const int row = pass * kRowsPerPass2 + lane / kLanesPerRow2;
       const int col = (lane % kLanesPerRow2) * 8;
       const int gi = i0 + row;
-      const int gj = j0 + wave * (kPaCols / kPaWaves) + col;
+      const int gj = j0 + ch * kPaChunk + wave * (kPaChunk / kPaWaves) + col;
       if (gi >= s || gj >= p.n) continue;
       const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(ep(row, col));
       const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(ep(row, col + 4));
@@ -982,12 +1044,15 @@ __global__ __launch_bounds__(kPaWaves * 64) void poly_apply_kernel(PolyApplyPara
       u32x4_t out;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float ax0 = p.a * bf16_to_f32(xe[pass][e] & 0xFFFFu);
-        const float ax1 = p.a * bf16_to_f32(xe[pass][e] >> 16);
+        const float ax0 = p.a * bf16_to_f32(xe[ch][pass][e] & 0xFFFFu);
+        const float ax1 = p.a * bf16_to_f32(xe[ch][pass][e] >> 16);
         out[e] = pack_bf16x2(ax0 + v[2 * e], ax1 + v[2 * e + 1]);
       }
       *reinterpret_cast<u32x4_t*>(Cb + (int64_t)gi * p.n + gj) = out;
     }
+    // the next chunk reuses this wave's staging rows
+    wait_lds();
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -1026,6 +1091,21 @@ hipError_t launch_gram(const uint16_t* x, uint16_t* a, float* trace_partials, co
       if (groups == 4)
         return launch<OP_GRAM, false, false, 32, 32, 1, 1, 2, kSmallBK, kSlab, 4>(p, sh.g, stream);
     }
+    // Too many one-wave tiles for one round: 64x64 tiles of 2x2 such blocks (64-deep slabs, the
+    // same 256-k groups) when those fit one round, each group on its own four waves.
+    constexpr int kSlab64 = kSmallGroupK / 64;
+    const int tiles_m64 = ceil_div(s, 64);
+    const int tiles64 = tiles_m64 * (tiles_m64 + 1) / 2;
+    if ((int64_t)p.tiles * sh.g > kCus && (int64_t)tiles64 * sh.g <= kCus && groups >= 2 &&
+        groups <= 4) {
+      p.tiles_m = p.tiles_n = tiles_m64;
+      p.tiles = tiles64;
+      if (groups == 2)
+        return launch<OP_GRAM, false, false, 64, 64, 2, 2, 2, 64, kSlab64, 2>(p, sh.g, stream);
+      if (groups == 3)
+        return launch<OP_GRAM, false, false, 64, 64, 2, 2, 2, 64, kSlab64, 3>(p, sh.g, stream);
+      return launch<OP_GRAM, false, false, 64, 64, 2, 2, 2, 64, kSlab64, 4>(p, sh.g, stream);
+    }
     return launch<OP_GRAM, false, false, 32, 32, 1, 1, 2, kSmallBK, kSlab>(p, sh.g, stream);
   }
   if (sh.tall())
@@ -1052,8 +1132,16 @@ hipError_t launch_poly(const uint16_t* a, uint16_t* bout, float coef_b, float co
   p.beta = coef_c;
   p.tiles_m = p.tiles_n = ceil_div(s, poly_tile(s));
   p.tiles = p.tiles_m * (p.tiles_m + 1) / 2;
-  if (poly_tile(s) == 32)
-    return launch<OP_POLY, false, false, 32, 32, 1, 1, 2, kSmallBK, 0>(p, g, stream);
+  if (poly_tile(s) == 32) {
+    if ((int64_t)p.tiles * g <= kCus)
+      return launch<OP_POLY, false, false, 32, 32, 1, 1, 2, kSmallBK, 0>(p, g, stream);
+    // more one-wave tiles than CUs: 64x64 tiles of four such waves (a quarter of the workgroups,
+    // each copying its operand rows once for four blocks); 3-9% shorter steps from 32 matrices of
+    // 256x768 up, the same below
+    p.tiles_m = p.tiles_n = ceil_div(s, 64);
+    p.tiles = p.tiles_m * (p.tiles_m + 1) / 2;
+    return launch<OP_POLY, false, false, 64, 64, 2, 2, 2, kSmallBK, 0>(p, g, stream);
+  }
   return launch<OP_POLY, false, false, 128, 128, 2, 4, 2, 64, 0>(p, g, stream);
 }
 
@@ -1129,28 +1217,59 @@ hipError_t launch_apply(const uint16_t* x, const uint16_t* bm, uint16_t* c, floa
   }
 }
 
-// The fused launch holds one workgroup per CU (82 KB of LDS) and forms each row block of B once
-// per column tile, so it pays only while its workgroups fit one round: measured on 256x768 it
-// beats the two launches up to 4 matrices (94.6 against 109.1 us alone) and loses from 8 on.
-bool poly_apply_fused(const Shape& sh) {
-  return !sh.tall() && sh.s() <= kPaMaxS && sh.m <= 1024 && apply_tiles(sh) == kApply32x128 &&
-         (int64_t)ceil_div(sh.m, kPaRows) * ceil_div(sh.n, kPaCols) * sh.g <= kCus;
+// The fused launch forms each 32-row block of B once per column tile, so it pays only while its
+// workgroups fit one round on the CUs: the column tile is the narrowest of 1, 2, 3 or 6 chunks
+// of 128 columns with which they do (one chunk: 82 KB of LDS; more: up to 147 KB, one workgroup
+// per CU).  Measured on 256x768 with one chunk it beats the two launches up to 4 matrices (94.6
+// against 109.1 us alone) and loses from 8 on, where it would form each block of B six times;
+// with 2 and 3 chunks the step is 7-10% shorter at 8 and 16 matrices.  Six chunks stream all of
+// X through each workgroup (512 KB per CU on 256x768), which the two launches beat unless every
+// CU is busy: 2% slower at 24 matrices (192 workgroups), 7% faster at 32 (256), so six chunks
+// are taken only when the launch fills at least 7/8 of the CUs.
+static int poly_apply_chunks(const Shape& sh) {
+  if (sh.tall() || sh.s() > kPaMaxS) return 0;
+  for (int nc : {1, 2, 3, 6}) {
+    const int64_t wgs = (int64_t)ceil_div(sh.m, kPaRows) * ceil_div(sh.n, kPaChunk * nc) * sh.g;
+    if (wgs <= kCus) return (nc < 6 || 8 * wgs >= 7 * kCus) ? nc : 0;
+  }
+  return 0;
 }
 
-hipError_t launch_poly_apply(const uint16_t* a, const uint16_t* x, uint16_t* c, float coef_a,
-                             float coef_b, float coef_c, const Shape& sh, hipStream_t stream) {
-  if (!poly_apply_fused(sh)) return hipErrorInvalidValue;
+bool poly_apply_fused(const Shape& sh) { return poly_apply_chunks(sh) > 0; }
+
+namespace {
+
+template <int NC>
+hipError_t launch_poly_apply_nc(const PolyApplyParams& p0, int64_t g, int m, int n,
+                                hipStream_t stream) {
+  using PC = PaCfg<NC>;
+  auto kern = poly_apply_kernel<NC>;
   static std::atomic<uint64_t> configured{0};
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   const uint64_t bit = dev < 64 ? (uint64_t(1) << dev) : 0;
   if (bit == 0 || !(configured.load(std::memory_order_acquire) & bit)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(poly_apply_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kPaLdsBytes);
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, PC::kLdsBytes);
     if (e != hipSuccess) return e;
     configured.fetch_or(bit, std::memory_order_release);
   }
+  PolyApplyParams p = p0;
+  p.tiles_n = ceil_div(n, PC::kCols);
+  p.tiles = ceil_div(m, kPaRows) * p.tiles_n;
+  // the tiles of the whole stack fit one round on the CUs, so the grid fits one launch
+  p.total = (int)(p.tiles * g);
+  hipLaunchKernelGGL(kern, dim3((unsigned)p.total), dim3(kPaWaves * 64), PC::kLdsBytes, stream,
+                     p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_poly_apply(const uint16_t* a, const uint16_t* x, uint16_t* c, float coef_a,
+                             float coef_b, float coef_c, const Shape& sh, hipStream_t stream) {
+  const int nc = poly_apply_chunks(sh);
   PolyApplyParams p{};
   p.A = a;
   p.X = x;
@@ -1160,13 +1279,18 @@ hipError_t launch_poly_apply(const uint16_t* a, const uint16_t* x, uint16_t* c, 
   p.a = coef_a;
   p.b = coef_b;
   p.c = coef_c;
-  p.tiles_n = ceil_div(sh.n, kPaCols);
-  p.tiles = ceil_div(sh.m, kPaRows) * p.tiles_n;
-  // g <= 256 here (the small-tile apply regime), so the grid fits one launch
-  p.total = (int)(p.tiles * sh.g);
-  hipLaunchKernelGGL(poly_apply_kernel, dim3((unsigned)p.total), dim3(kPaWaves * 64), kPaLdsBytes,
-                     stream, p);
-  return hipGetLastError();
+  switch (nc) {
+    case 1:
+      return launch_poly_apply_nc<1>(p, sh.g, sh.m, sh.n, stream);
+    case 2:
+      return launch_poly_apply_nc<2>(p, sh.g, sh.m, sh.n, stream);
+    case 3:
+      return launch_poly_apply_nc<3>(p, sh.g, sh.m, sh.n, stream);
+    case 6:
+      return launch_poly_apply_nc<6>(p, sh.g, sh.m, sh.n, stream);
+    default:
+      return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace anvil

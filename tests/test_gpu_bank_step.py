@@ -177,11 +177,16 @@ def test_deterministic_and_batch_invariant(gpu_lib, g, m, n):
         assert torch.equal(one.view(torch.int16), whole[i:i + 1].view(torch.int16))
 
 
-@pytest.mark.parametrize("g,m,n", [(24, 256, 768), (44, 200, 328), (66, 136, 136)])
+@pytest.mark.parametrize("g,m,n", [(44, 200, 328), (66, 136, 136), (16, 200, 328),
+                                   (24, 200, 328), (32, 200, 696), (24, 256, 768)])
 def test_fused_poly_apply_matches_stack(gpu_lib, g, m, n):
     """Small wide matrices stepped alone form B inside the apply's launch (one launch per map
-    instead of two); in a stack this large the polynomial and the apply run as separate kernels
-    with 128x128 apply tiles.  Each matrix's step must be the same bit for bit either way."""
+    instead of two, column tiles of one 128-column chunk).  Stacks (44, 200, 328), (66, 136, 136)
+    and (24, 256, 768) run the polynomial and the apply as separate kernels (the first and last
+    with 64x64 polynomial tiles, the last with the Gram's k groups on separate waves of 64x64
+    tiles); the others take the fused launch with column tiles of 2, 3 and 6 chunks (the last
+    column tile ragged where n is not a multiple of the tile).  Each matrix's step must be the
+    same bit for bit either way."""
     import torch
     G = to_gpu_f32(_gauss_steps(g, m, n, 21, 1)[0])
     vs = torch.randn((2, g, m, n), dtype=torch.float32, device="cuda")
