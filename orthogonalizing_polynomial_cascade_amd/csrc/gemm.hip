@@ -294,6 +294,11 @@ struct Cfg {
   static_assert(kLoadsPerSlab * (STAGES - 2) < 64, "vmcnt range");
 };
 
+// The four-wave Gram tiles run two workgroups per CU, two waves per SIMD: they may take up to 256
+// registers per lane, which their read-ahead of a whole slab's fragments needs.
+template <int OP, int WAVES, int KSPLIT>
+constexpr int kMinWavesPerEu = OP == OP_GRAM && WAVES == 4 && KSPLIT == 1 ? 2 : 1;
+
 // KSPLIT > 1 (Gram tiles with slab groups only): the tile's KSPLIT slab groups go to KSPLIT sets
 // of WM x WN waves, each set with its own ring, which accumulate one group each from zero; the
 // group sums are then added to the first set's in group order, which is exactly the unsplit
@@ -303,7 +308,9 @@ struct Cfg {
 // wave block, the partials of 32x32 tiles.
 template <int OP, bool PT, bool QT, int BM, int BN, int WM, int WN, int STAGES, int BK, int SLAB,
           int KSPLIT = 1>
-__global__ __launch_bounds__(WM * WN * KSPLIT * 64) void gemm_kernel(GemmParams p) {
+__global__ __launch_bounds__(WM * WN * KSPLIT * 64)
+__attribute__((amdgpu_waves_per_eu(kMinWavesPerEu<OP, WM * WN, KSPLIT>)))
+void gemm_kernel(GemmParams p) {
   using C = Cfg<BM, BN, WM, WN, STAGES, BK>;
   static_assert(KSPLIT == 1 || (OP == OP_GRAM && SLAB > 0 && STAGES == 2),
                 "k groups over waves: Gram tiles with slab groups and two stages");
@@ -443,10 +450,11 @@ __global__ __launch_bounds__(WM * WN * KSPLIT * 64) void gemm_kernel(GemmParams 
     }
     // Fragments of the whole slab are read before its multiplies when a wave holds at most two
     // fragments (its MFMAs then form one or two dependent chains, and reading per k-step would
-    // put an LDS round trip in front of every MFMA); larger wave tiles read per k-step, which
-    // keeps their registers within the two workgroups per CU (reading ahead there made the
-    // 128x256 apply 140 registers and the mlp step 25% slower).
-    constexpr bool kHoist = C::kFM * C::kFN <= 2;
+    // put an LDS round trip in front of every MFMA), and in the Gram, whose four waves per
+    // workgroup leave room for them (mlp Gram 63.5 -> 60.5 us).  The apply's and polynomial's
+    // larger wave tiles read per k-step, which keeps their registers within four waves per SIMD
+    // (reading ahead there made the 128x256 apply 140 registers and the mlp step 25% slower).
+    constexpr bool kHoist = C::kFM * C::kFN <= 2 || OP == OP_GRAM;
     constexpr int kKs = BK / 16;
     bf16x8_t fa[kKs][C::kFM], fb[kKs][C::kFN];
 #pragma unroll
