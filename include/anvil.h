@@ -157,7 +157,8 @@ int anvil_momentum(const float* grad, float* velocity, float momentum, float fas
                    void* stream);
 
 /* Number of fp32 trace partials per matrix that anvil_gram writes for shape m x n: one per
- * diagonal tile of the Gram, whose tile size depends on the shape (0 for an unsupported shape). */
+ * 32-row block of the Gram's diagonal when min(m, n) <= 256 and m <= n, else one per 128-row
+ * block (0 for an unsupported shape). */
 int64_t anvil_trace_slots(int64_t m, int64_t n);
 
 /* Gram (step 3): a_out bf16 [g,s,s] = bf16(X^T X) if tall else bf16(X X^T), fp32 accumulation,
