@@ -1,7 +1,9 @@
 """Per-stage parity of the HIP kernels against the oracle, through the C ABI stage entry points.
 
 Shapes span several 128-wide tiles with ragged edges, both orientations, the square case and the
-split threshold."""
+split threshold; the last two are stacks of small wide matrices whose 32x32 Gram and polynomial
+tiles would outnumber the CUs, so they take 64x64 tiles (the Gram with its 256-k groups on
+separate sets of waves: two groups with a ragged last slab, and three)."""
 import numpy as np
 import pytest
 
@@ -12,7 +14,8 @@ from tests.helpers import (assert_gemm_close, bf16_bits_of, from_gpu, oracle_nor
 pytestmark = pytest.mark.gpu
 
 SHAPES = [(3, 200, 328), (3, 392, 136), (2, 264, 264), (2, 1096, 136), (2, 136, 1096),
-          (1, 8, 8), (2, 8, 72), (2, 72, 8), (1, 256, 768), (1, 768, 256)]
+          (1, 8, 8), (2, 8, 72), (2, 72, 8), (1, 256, 768), (1, 768, 256), (10, 200, 328),
+          (12, 256, 768)]
 
 
 @pytest.mark.parametrize("g,m,n", SHAPES)
