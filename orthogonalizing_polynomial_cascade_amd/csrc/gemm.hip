@@ -72,6 +72,8 @@ namespace {
 enum { OP_GRAM = 0, OP_POLY = 1, OP_APPLY = 2 };
 
 constexpr uint32_t kOOB = 0x80000000u;   // buffer offset past any range: the load returns 0
+constexpr int kCus = 256;                // compute units of the MI355X (8 XCDs of 32)
+constexpr int kFullRound = 512;          // two workgroups per CU
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x8_t __attribute__((ext_vector_type(8)));
@@ -100,6 +102,7 @@ struct GemmParams {
   int tiles;                  // tiles per matrix (upper triangle for Gram and poly)
   int total;                  // tiles * g
   int split;
+  int pair_diagonals;         // symmetric product of one to two rounds: see diagonal_first
 };
 
 // ---------------------------------------------------------------------------------------------
@@ -272,6 +275,50 @@ __device__ __forceinline__ void upper_tile(int t, int tiles, int* ti, int* tj) {
   *tj = i + t;
 }
 
+// Diagonal tiles of an upper-triangle tile grid (tiles_m tiles per side, tiles = tiles_m(tiles_m+1)/2
+// per matrix, row by row): the diagonal tile of row i sits at t = i*tiles_m - i(i-1)/2.
+__device__ __forceinline__ int diag_pos(int i, int tiles_m) { return i * tiles_m - i * (i - 1) / 2; }
+
+// Number of diagonal tiles with logical id below L (matrices one after the other).
+__device__ __forceinline__ int diagonals_before(int L, int tiles, int tiles_m) {
+  const int t = L % tiles;
+  int i = 0;
+  while (i < tiles_m && diag_pos(i, tiles_m) < t) ++i;
+  return (L / tiles) * tiles_m + i;
+}
+
+// Gram launches with one to two rounds of workgroups: the first round puts one workgroup on every
+// CU of an XCD (32 per XCD) and each later workgroup of the XCD shares a CU with one of the first
+// (observed: workgroup 32+k of an XCD joins the CU of workgroup k).  A CU
+// holding two workgroups sets the launch's time, so those slots take the XCD's cheaper diagonal
+// tiles (one operand copy, a wave fewer multiplying) first: workgroup `local` of an XCD whose
+// logical range is [start, start + count) gets the rank-th tile of the range in diagonal-first
+// order, where the shared slots (0..p-1 and 32..count-1, p = count - 32) come first.  The result
+// is a permutation of the range; which tile a workgroup takes changes no arithmetic.
+__device__ __forceinline__ int diagonal_first(int start, int count, int local, int tiles,
+                                              int tiles_m) {
+  constexpr int kCusPerXcd = 32;
+  const int p = count > kCusPerXcd ? count - kCusPerXcd : 0;
+  const int rank = local < p ? local
+                   : local >= kCusPerXcd ? p + (local - kCusPerXcd)
+                                         : 2 * p + (local - p);
+  const int d0 = diagonals_before(start, tiles, tiles_m);
+  const int nd = diagonals_before(start + count, tiles, tiles_m) - d0;
+  if (rank < nd) {
+    const int gd = d0 + rank;
+    return (gd / tiles_m) * tiles + diag_pos(gd % tiles_m, tiles_m);
+  }
+  const int offs = tiles - tiles_m;   // off-diagonal tiles per matrix (> 0 here)
+  const int go = (start - d0) + (rank - nd);
+  int k = go % offs;
+  int i = 0;
+  while (k >= tiles_m - 1 - i) {
+    k -= tiles_m - 1 - i;
+    ++i;
+  }
+  return (go / offs) * tiles + diag_pos(i, tiles_m) + 1 + k;
+}
+
 template <int BM, int BN, int WM, int WN, int STAGES, int BK>
 struct Cfg {
   static constexpr int kWaves = WM * WN;
@@ -329,7 +376,14 @@ void gemm_kernel(GemmParams p) {
   const int wm = wave / WN;
   const int wn = wave % WN;
 
-  const int logical = xcd_remap(blockIdx.x, p.total);
+  int logical = xcd_remap(blockIdx.x, p.total);
+  if (OP == OP_GRAM && p.pair_diagonals) {
+    constexpr int kXcd = 8;
+    const int x = blockIdx.x % kXcd;
+    const int q = p.total / kXcd, r = p.total % kXcd;
+    const int start = x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q;
+    logical = diagonal_first(start, q + (x < r ? 1 : 0), blockIdx.x / kXcd, p.tiles, p.tiles_m);
+  }
   const int64_t b = logical / p.tiles;
   const int t = logical % p.tiles;
   int ti, tj;
@@ -758,6 +812,12 @@ hipError_t launch(GemmParams p, int64_t g, hipStream_t stream) {
     if (q.E) q.E += b0 * p.strideE;
     if (q.trace) q.trace += b0 * p.trace_slots;
     q.total = (int)(p.tiles * gb);
+    // Gram launches of one to two rounds whose diagonal tiles can fill every shared CU (the Vs
+    // and Us Grams: 320 tiles, 128 of them diagonal, 9% / 5% shorter); the polynomial's diagonal
+    // tiles are not the cheaper ones (their epilogue costs twice an off-diagonal one's at K = s),
+    // and there pairing them was 8-12% slower
+    q.pair_diagonals = OP == OP_GRAM && q.total > kCus && q.total <= kFullRound &&
+                       gb * p.tiles_m >= 2 * (q.total - kCus);
     hipLaunchKernelGGL(kern, dim3((unsigned)q.total), dim3(kThreads), kLdsBytes, stream, q);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -799,8 +859,6 @@ constexpr int kSmallGroupK = 256;
 #define ANVIL_SLAB_GROUP 8
 #endif
 constexpr int kGramSlabGroup = ANVIL_SLAB_GROUP;   // in 64-deep slabs: 512 k
-constexpr int kFullRound = 512;
-constexpr int kCus = 256;
 
 
 // ---------------------------------------------------------------------------------------------
