@@ -27,8 +27,9 @@
 // operands: it copies them once, and its waves whose block lies wholly below the diagonal skip
 // their multiplies.
 //
-// For a few small wide matrices (s <= 256) poly_apply_kernel runs a map's polynomial and apply as
-// one launch, each workgroup forming the rows of B its tile needs (same bits as the two kernels).
+// For stacks of small wide matrices (s <= 256) whose tiles fit one round on the CUs,
+// poly_apply_kernel runs a map's polynomial and apply as one launch, each workgroup forming the
+// rows of B its tile needs (same bits as the two kernels).
 //
 // Pipeline (CDNA4 / gfx950):
 //  * Operand slabs (rows x BK k, BK = 32, 64 or 128) travel HBM -> LDS with
@@ -43,12 +44,15 @@
 //    read: within a 16-lane group, lanes 4j..4j+3 point at 16 consecutive rows of k-row j and
 //    lane r receives the 4 k-values of row r.  No VALU transposes.
 //  * Each wave owns a (BM/WM) x (BN/WN) block of 32x32 MFMA fragments.  In the Gram, each group
-//    of 8 slabs (512 k) is accumulated into fresh registers and then added to the running sums
-//    with IEEE fp32 adds (one MFMA accumulation chain over thousands of k drifts from an fp64
-//    reference noticeably more than sgemm on low-rank-dominated inputs); the polynomial and the
-//    apply (K = the short side) accumulate directly.
+//    of 512 k (256 k for s <= 256) is accumulated into fresh registers and then added to the
+//    running sums with IEEE fp32 adds (one MFMA accumulation chain over thousands of k drifts
+//    from an fp64 reference noticeably more than sgemm on low-rank-dominated inputs); small
+//    Grams may give the groups of a tile to separate sets of waves and add their sums in group
+//    order, which is the same arithmetic.  The polynomial and the apply (K = the short side)
+//    accumulate directly.
 //  * Tiles are ordered so that consecutive tiles of one matrix land on the same XCD (hardware
-//    dispatches workgroups round-robin over the 8 XCDs, each with its own L2).
+//    dispatches workgroups round-robin over the 8 XCDs, each with its own L2); a Gram launch of
+//    one to two rounds puts its diagonal tiles on the CUs that hold two workgroups.
 //  * The epilogue goes through LDS, 32 rows at a time per wave: rows leave as 16-byte stores, and
 //    the mirror of a symmetric tile is read down the LDS columns and leaves as 16-byte stores,
 //    four lanes per mirrored row.
