@@ -3,7 +3,8 @@
 Shapes span several 128-wide tiles with ragged edges, both orientations, the square case and the
 split threshold; the last two are stacks of small wide matrices whose 32x32 Gram and polynomial
 tiles would outnumber the CUs, so they take 64x64 tiles (the Gram with its 256-k groups on
-separate sets of waves: two groups with a ragged last slab, and three)."""
+separate sets of waves: two groups with a ragged last slab, and three).  The 44-matrix stack's
+Gram (264 tiles, 132 diagonal) gives the CU-sharing workgroup slots to its diagonal tiles."""
 import numpy as np
 import pytest
 
@@ -15,7 +16,7 @@ pytestmark = pytest.mark.gpu
 
 SHAPES = [(3, 200, 328), (3, 392, 136), (2, 264, 264), (2, 1096, 136), (2, 136, 1096),
           (1, 8, 8), (2, 8, 72), (2, 72, 8), (1, 256, 768), (1, 768, 256), (10, 200, 328),
-          (12, 256, 768)]
+          (12, 256, 768), (44, 392, 264)]
 
 
 @pytest.mark.parametrize("g,m,n", SHAPES)
