@@ -26,7 +26,8 @@ struct Shape {
   int L() const { return m > n ? m : n; }
 };
 
-// Number of diagonal tiles of the Gram (trace partials per matrix).
+// Trace partials per matrix that launch_gram writes: one per 32-row diagonal block for wide or
+// square shapes with s <= 256, else one per 128-row diagonal tile.
 int gram_trace_slots(const Shape& sh);
 
 hipError_t launch_gram(const uint16_t* x, uint16_t* a, float* trace_partials, const Shape& sh,
@@ -38,8 +39,9 @@ hipError_t launch_poly(const uint16_t* a, uint16_t* b, float coef_b, float coef_
 hipError_t launch_apply(const uint16_t* x, const uint16_t* b, uint16_t* c, float coef_a,
                         bool split, const Shape& sh, hipStream_t stream);
 // Polynomial and apply of one map in a single launch (C = a X + B X with B = b A + c A·A formed
-// per tile), for the wide shapes whose apply takes the small-tile configuration (s <= 256, few
-// matrices); the same arithmetic as launch_poly followed by launch_apply, element for element.
+// per tile), for wide or square shapes with s <= 256 whose tiles of 32 rows by 1, 2, 3 or 6
+// chunks of 128 columns fit one round on the CUs; the same arithmetic as launch_poly followed by
+// launch_apply, element for element.
 bool poly_apply_fused(const Shape& sh);
 hipError_t launch_poly_apply(const uint16_t* a, const uint16_t* x, uint16_t* c, float coef_a,
                              float coef_b, float coef_c, const Shape& sh, hipStream_t stream);
