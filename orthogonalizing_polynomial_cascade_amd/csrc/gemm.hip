@@ -896,35 +896,42 @@ constexpr int kPaRows = 32;         // tile rows (rows of B and of C)
 constexpr int kPaChunk = 128;       // columns of C per chunk; a tile is NC chunks
 constexpr int kPaMaxS = 256;
 constexpr int kPaBK = 64;
-constexpr int kPaWaves = 4;
 constexpr int kPaBsBytes = kPaRows * kPaMaxS * 2;                       // 16 KB: A, then B, rows
 constexpr int kPaStage1 = kPaMaxS * kPaBK * 2;                          // 32 KB: all rows of A
-constexpr int kPaEpi1Pitch = kPaMaxS / kPaWaves + 4;                    // fp32 per staged row
-constexpr int kPaEpi2Pitch = kPaChunk / kPaWaves + 4;
-constexpr int kPaEpi1Bytes = kPaWaves * kPaRows * kPaEpi1Pitch * 4;     // 34.8 KB
-constexpr int kPaRing2 = kPaBsBytes + kPaEpi1Bytes;                     // phase-2 ring offset
-static_assert(kPaRing2 % 16 == 0, "16-byte aligned phase-2 ring");
-static_assert(kPaBsBytes + kPaWaves * kPaRows * kPaEpi2Pitch * 4 <= kPaRing2,
-              "phase-2 staging below the phase-2 ring");
+constexpr int kPaEpi2Pitch = 32 + 4;                                    // fp32 per staged row
 
-// A tile of NC chunks of 128 columns: wave w owns columns 32w..32w+31 of every chunk.  The X
-// slabs of the chunks sit side by side in a stage (64 deep, or 32 deep for more than three
-// chunks, so that two stages fit beside the rows of B and the phase-1 staging).
-template <int NC>
+// A tile of NC chunks of 128 columns, W = 4 or 8 waves: wave w owns columns 32(w % 4) .. +31 of
+// chunks w / 4, w / 4 + W / 4, ... (every chunk with four waves, every other one with eight).
+// In phase 1 wave w forms columns (256 / W) w .. of the 32 rows of B.  The X slabs of the chunks
+// sit side by side in a stage (64 deep, or 32 deep for more than three chunks, so that two
+// stages fit beside the rows of B and the phase-1 staging).
+template <int NC, int W>
 struct PaCfg {
+  static_assert(W == 4 || W == 8, "four or eight waves");
+  static_assert(NC % (W / 4) == 0, "whole chunks per wave");
+  static constexpr int kWaves = W;
+  static constexpr int kChunkStep = W / 4;          // chunks between a wave's chunks
+  static constexpr int kOwn = NC / kChunkStep;      // chunks per wave
   static constexpr int kCols = kPaChunk * NC;
   static constexpr int kBK2 = NC <= 3 ? 64 : 32;
   static constexpr int kChunkBytes = kPaChunk * kBK2 * 2;
   static constexpr int kStage2 = NC * kChunkBytes;
+  static constexpr int kEpi1Pitch = kPaMaxS / W + 4;                       // fp32 per staged row
+  static constexpr int kEpi1Bytes = W * kPaRows * kEpi1Pitch * 4;          // 34.8 / 36.9 KB
+  static constexpr int kRing2 = kPaBsBytes + kEpi1Bytes;                   // phase-2 ring offset
   static constexpr int kLdsBytes =
-      kPaBsBytes + (2 * kPaStage1 > kPaEpi1Bytes + 2 * kStage2 ? 2 * kPaStage1
-                                                               : kPaEpi1Bytes + 2 * kStage2);
+      kPaBsBytes + (2 * kPaStage1 > kEpi1Bytes + 2 * kStage2 ? 2 * kPaStage1
+                                                             : kEpi1Bytes + 2 * kStage2);
+  static_assert(kRing2 % 16 == 0, "16-byte aligned phase-2 ring");
+  static_assert(kPaBsBytes + W * kPaRows * kPaEpi2Pitch * 4 <= kRing2,
+                "phase-2 staging below the phase-2 ring");
   static_assert(kLdsBytes <= 160 * 1024, "LDS of one CU");
 };
 
-template <int NC>
-__global__ __launch_bounds__(kPaWaves * 64) void poly_apply_kernel(PolyApplyParams p) {
-  using PC = PaCfg<NC>;
+template <int NC, int W>
+__global__ __launch_bounds__(W * 64) void poly_apply_kernel(PolyApplyParams p) {
+  using PC = PaCfg<NC, W>;
+  constexpr int kWaves = W;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -946,13 +953,13 @@ __global__ __launch_bounds__(kPaWaves * 64) void poly_apply_kernel(PolyApplyPara
   using BsLayout = KContig<kPaRows, kPaMaxS>;
   const uint32_t lds0 = lds_addr(smem);
   const uint32_t ring1 = lds0 + kPaBsBytes;
-  const uint32_t ring2 = lds0 + kPaRing2;
+  const uint32_t ring2 = lds0 + PC::kRing2;
 
   // rows i0..i0+31 of A into Bs: instruction u (1 KB) holds rows 2u, 2u+1, lane L row 2u + L/32,
   // physical slot L%32 = logical slot (L%32) ^ swizzle(row); zeros past s
 #pragma unroll
-  for (int q = 0; q < kPaRows / 2 / kPaWaves; ++q) {
-    const int u = wave + q * kPaWaves;
+  for (int q = 0; q < kPaRows / 2 / kWaves; ++q) {
+    const int u = wave + q * kWaves;
     const int row = 2 * u + (lane >> 5);
     const int c = (lane & 31) ^ BsLayout::swz(row);
     const int gr = i0 + row;
@@ -960,26 +967,28 @@ __global__ __launch_bounds__(kPaWaves * 64) void poly_apply_kernel(PolyApplyPara
     dma16(rA, lds0 + (uint32_t)u * 1024u, voff);
   }
   // phase 1: the slabs of all rows of A (K-contiguous, 64 deep)
-  const SlabCopy<false, kPaMaxS, kPaBK, kPaWaves> copyQ1(s, 0, s, wave, lane);
-  constexpr int kFn1 = kPaMaxS / kPaWaves / 32;                      // 2 fragments per wave
+  const SlabCopy<false, kPaMaxS, kPaBK, kWaves> copyQ1(s, 0, s, wave, lane);
+  constexpr int kFn1 = kPaMaxS / kWaves / 32;                 // 2 fragments per wave (1 of 8)
   const int KT = (s + kPaBK - 1) / kPaBK;
   copyQ1.issue(rA, ring1, 0, s, wave);
 
   // the X values of this wave's part of the final epilogue, fetched now (8 columns per lane)
-  constexpr int kLanesPerRow2 = (kPaChunk / kPaWaves) / 8;  // 4
+  constexpr int kLanesPerRow2 = 32 / 8;                      // 4
   constexpr int kRowsPerPass2 = 64 / kLanesPerRow2;         // 16
   constexpr int kPasses2 = kPaRows / kRowsPerPass2;         // 2
-  u32x4_t xe[NC][kPasses2];
+  const int cg = wave % 4;                                   // column group inside a chunk
+  const int c0 = wave / 4;                                   // this wave's first chunk
+  u32x4_t xe[PC::kOwn][kPasses2];
 #pragma unroll
-  for (int ch = 0; ch < NC; ++ch)
+  for (int o = 0; o < PC::kOwn; ++o)
 #pragma unroll
     for (int pass = 0; pass < kPasses2; ++pass) {
+      const int ch = c0 + o * PC::kChunkStep;
       const int gi = i0 + pass * kRowsPerPass2 + lane / kLanesPerRow2;
-      const int gj =
-          j0 + ch * kPaChunk + wave * (kPaChunk / kPaWaves) + (lane % kLanesPerRow2) * 8;
-      xe[ch][pass] = (gi < s && gj < p.n)
-                         ? *reinterpret_cast<const u32x4_t*>(Xb + (int64_t)gi * p.n + gj)
-                         : u32x4_t{0u, 0u, 0u, 0u};
+      const int gj = j0 + ch * kPaChunk + cg * 32 + (lane % kLanesPerRow2) * 8;
+      xe[o][pass] = (gi < s && gj < p.n)
+                        ? *reinterpret_cast<const u32x4_t*>(Xb + (int64_t)gi * p.n + gj)
+                        : u32x4_t{0u, 0u, 0u, 0u};
     }
 
   f32x16_t acc1[kFn1];
@@ -999,7 +1008,7 @@ __global__ __launch_bounds__(kPaWaves * 64) void poly_apply_kernel(PolyApplyPara
 #pragma unroll
       for (int f = 0; f < kFn1; ++f) {
         const bf16x8_t fb =
-            read_frag<false, kPaMaxS, kPaBK>(tq, wave * (kPaMaxS / kPaWaves) + f * 32, ks, lane);
+            read_frag<false, kPaMaxS, kPaBK>(tq, wave * (kPaMaxS / kWaves) + f * 32, ks, lane);
         acc1[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb, fa, acc1[f], 0, 0, 0);
       }
     }
@@ -1007,7 +1016,7 @@ __global__ __launch_bounds__(kPaWaves * 64) void poly_apply_kernel(PolyApplyPara
   __syncthreads();   // the ring and the A rows are read: stage the accumulators, load X
 
   // the X slabs of the chunks (chunk ch at ch * kChunkBytes of a stage)
-  using Copy2 = SlabCopy<true, kPaChunk, PC::kBK2, kPaWaves>;
+  using Copy2 = SlabCopy<true, kPaChunk, PC::kBK2, kWaves>;
   Copy2 copyQ2[NC];
 #pragma unroll
   for (int ch = 0; ch < NC; ++ch) copyQ2[ch] = Copy2(p.n, j0 + ch * kPaChunk, p.n, wave, lane);
@@ -1021,8 +1030,8 @@ __global__ __launch_bounds__(kPaWaves * 64) void poly_apply_kernel(PolyApplyPara
   // phase-1 epilogue: B = b*A + c*(A*A), rounded to bf16, in place of A in Bs (each lane reads
   // the A piece it then overwrites; zeros past column s)
   {
-    float* epi = reinterpret_cast<float*>(smem + kPaBsBytes) + wave * kPaRows * kPaEpi1Pitch;
-    auto ep = [&](int row, int col) { return epi + row * kPaEpi1Pitch + (col ^ (row & 16)); };
+    float* epi = reinterpret_cast<float*>(smem + kPaBsBytes) + wave * kPaRows * PC::kEpi1Pitch;
+    auto ep = [&](int row, int col) { return epi + row * PC::kEpi1Pitch + (col ^ (row & 16)); };
 #pragma unroll
     for (int f = 0; f < kFn1; ++f)
 #pragma unroll
@@ -1034,13 +1043,13 @@ __global__ __launch_bounds__(kPaWaves * 64) void poly_apply_kernel(PolyApplyPara
       }
     wait_lds();
     __builtin_amdgcn_wave_barrier();
-    constexpr int kLanesPerRow = (kPaMaxS / kPaWaves) / 8;   // 8
+    constexpr int kLanesPerRow = (kPaMaxS / kWaves) / 8;   // 8 (four waves), 4 (eight)
     constexpr int kRowsPerPass = 64 / kLanesPerRow;           // 8
 #pragma unroll
     for (int pass = 0; pass < kPaRows / kRowsPerPass; ++pass) {
       const int row = pass * kRowsPerPass + lane / kLanesPerRow;
       const int col = (lane % kLanesPerRow) * 8;
-      const int j = wave * (kPaMaxS / kPaWaves) + col;       // column of B (k of phase 2)
+      const int j = wave * (kPaMaxS / kWaves) + col;       // column of B (k of phase 2)
       u32x4_t* piece = reinterpret_cast<u32x4_t*>(Bs + BsLayout::offset(row, j / 8));
       const u32x4_t ae = *piece;
       const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(ep(row, col));
@@ -1065,24 +1074,25 @@ __global__ __launch_bounds__(kPaWaves * 64) void poly_apply_kernel(PolyApplyPara
   // ---- phase 2: C = a X + B X on the chunks' columns (wave w: 32w .. 32w+31 of each), K = s ----
   constexpr int kKs2 = PC::kBK2 / 16;
   const int KT2 = (s + PC::kBK2 - 1) / PC::kBK2;
-  f32x16_t acc2[NC];
+  f32x16_t acc2[PC::kOwn];
 #pragma unroll
-  for (int ch = 0; ch < NC; ++ch)
+  for (int o = 0; o < PC::kOwn; ++o)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc2[ch][r] = 0.0f;
+    for (int r = 0; r < 16; ++r) acc2[o][r] = 0.0f;
   for (int kt = 0; kt < KT2; ++kt) {
     wait_vmcnt<0>();
     __syncthreads();
     if (kt + 1 < KT2) issue2(ring2 + (uint32_t)(((kt + 1) & 1) * PC::kStage2), (kt + 1) * PC::kBK2);
-    const char* tq = smem + kPaRing2 + (kt & 1) * PC::kStage2;
+    const char* tq = smem + PC::kRing2 + (kt & 1) * PC::kStage2;
 #pragma unroll
     for (int ks = 0; ks < kKs2; ++ks) {
       const bf16x8_t fa = read_frag<false, kPaRows, kPaMaxS>(Bs, 0, kt * kKs2 + ks, lane);
 #pragma unroll
-      for (int ch = 0; ch < NC; ++ch) {
-        const bf16x8_t fb = read_frag<true, kPaChunk, PC::kBK2>(
-            tq + ch * PC::kChunkBytes, wave * (kPaChunk / kPaWaves), ks, lane);
-        acc2[ch] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb, fa, acc2[ch], 0, 0, 0);
+      for (int o = 0; o < PC::kOwn; ++o) {
+        const int ch = c0 + o * PC::kChunkStep;
+        const bf16x8_t fb = read_frag<true, kPaChunk, PC::kBK2>(tq + ch * PC::kChunkBytes,
+                                                                cg * 32, ks, lane);
+        acc2[o] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb, fa, acc2[o], 0, 0, 0);
       }
     }
   }
@@ -1091,13 +1101,14 @@ __global__ __launch_bounds__(kPaWaves * 64) void poly_apply_kernel(PolyApplyPara
   float* epi = reinterpret_cast<float*>(smem + kPaBsBytes) + wave * kPaRows * kPaEpi2Pitch;
   auto ep = [&](int row, int col) { return epi + row * kPaEpi2Pitch + (col ^ (row & 16)); };
 #pragma unroll
-  for (int ch = 0; ch < NC; ++ch) {
+  for (int o = 0; o < PC::kOwn; ++o) {
+    const int ch = c0 + o * PC::kChunkStep;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int row = lane & 31;
       const int col = 8 * q + 4 * (lane >> 5);
       *reinterpret_cast<f32x4_t*>(ep(row, col)) =
-          f32x4_t{acc2[ch][4 * q], acc2[ch][4 * q + 1], acc2[ch][4 * q + 2], acc2[ch][4 * q + 3]};
+          f32x4_t{acc2[o][4 * q], acc2[o][4 * q + 1], acc2[o][4 * q + 2], acc2[o][4 * q + 3]};
     }
     wait_lds();
     __builtin_amdgcn_wave_barrier();
@@ -1106,7 +1117,7 @@ __global__ __launch_bounds__(kPaWaves * 64) void poly_apply_kernel(PolyApplyPara
       const int row = pass * kRowsPerPass2 + lane / kLanesPerRow2;
       const int col = (lane % kLanesPerRow2) * 8;
       const int gi = i0 + row;
-      const int gj = j0 + ch * kPaChunk + wave * (kPaChunk / kPaWaves) + col;
+      const int gj = j0 + ch * kPaChunk + cg * 32 + col;
       if (gi >= s || gj >= p.n) continue;
       const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(ep(row, col));
       const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(ep(row, col + 4));
@@ -1114,8 +1125,8 @@ __global__ __launch_bounds__(kPaWaves * 64) void poly_apply_kernel(PolyApplyPara
       u32x4_t out;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float ax0 = p.a * bf16_to_f32(xe[ch][pass][e] & 0xFFFFu);
-        const float ax1 = p.a * bf16_to_f32(xe[ch][pass][e] >> 16);
+        const float ax0 = p.a * bf16_to_f32(xe[o][pass][e] & 0xFFFFu);
+        const float ax1 = p.a * bf16_to_f32(xe[o][pass][e] >> 16);
         out[e] = pack_bf16x2(ax0 + v[2 * e], ax1 + v[2 * e + 1]);
       }
       *reinterpret_cast<u32x4_t*>(Cb + (int64_t)gi * p.n + gj) = out;
@@ -1289,19 +1300,17 @@ hipError_t launch_apply(const uint16_t* x, const uint16_t* bm, uint16_t* c, floa
 
 // The fused launch forms each 32-row block of B once per column tile, so it pays only while its
 // workgroups fit one round on the CUs: the column tile is the narrowest of 1, 2, 3 or 6 chunks
-// of 128 columns with which they do (one chunk: 82 KB of LDS; more: up to 147 KB, one workgroup
+// of 128 columns with which they do (one chunk: 82 KB of LDS; more: up to 149 KB, one workgroup
 // per CU).  Measured on 256x768 with one chunk it beats the two launches up to 4 matrices (94.6
-// against 109.1 us alone) and loses from 8 on, where it would form each block of B six times;
-// with 2 and 3 chunks the step is 7-10% shorter at 8 and 16 matrices.  Six chunks stream all of
-// X through each workgroup (512 KB per CU on 256x768), which the two launches beat unless every
-// CU is busy: 2% slower at 24 matrices (192 workgroups), 7% faster at 32 (256), so six chunks
-// are taken only when the launch fills at least 7/8 of the CUs.
+// against 109.1 us alone) and loses from 8 on, where it would form each block of B six times.
+// Tiles of an even number of chunks run eight waves (two waves per SIMD; each wave owns every
+// other chunk), which took the step from 100.9 to 96.1 us at 8 matrices (2 chunks) and from 204.1
+// to 194.3 us at 32 (6 chunks); with four waves six chunks lost to the two launches at 24
+// matrices (165.8 against 159.4 us), with eight they win (152.1).
 static int poly_apply_chunks(const Shape& sh) {
   if (sh.tall() || sh.s() > kPaMaxS) return 0;
-  for (int nc : {1, 2, 3, 6}) {
-    const int64_t wgs = (int64_t)ceil_div(sh.m, kPaRows) * ceil_div(sh.n, kPaChunk * nc) * sh.g;
-    if (wgs <= kCus) return (nc < 6 || 8 * wgs >= 7 * kCus) ? nc : 0;
-  }
+  for (int nc : {1, 2, 3, 6})
+    if ((int64_t)ceil_div(sh.m, kPaRows) * ceil_div(sh.n, kPaChunk * nc) * sh.g <= kCus) return nc;
   return 0;
 }
 
@@ -1309,11 +1318,11 @@ bool poly_apply_fused(const Shape& sh) { return poly_apply_chunks(sh) > 0; }
 
 namespace {
 
-template <int NC>
+template <int NC, int W = 4>
 hipError_t launch_poly_apply_nc(const PolyApplyParams& p0, int64_t g, int m, int n,
                                 hipStream_t stream) {
-  using PC = PaCfg<NC>;
-  auto kern = poly_apply_kernel<NC>;
+  using PC = PaCfg<NC, W>;
+  auto kern = poly_apply_kernel<NC, W>;
   static std::atomic<uint64_t> configured{0};
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -1330,8 +1339,7 @@ hipError_t launch_poly_apply_nc(const PolyApplyParams& p0, int64_t g, int m, int
   p.tiles = ceil_div(m, kPaRows) * p.tiles_n;
   // the tiles of the whole stack fit one round on the CUs, so the grid fits one launch
   p.total = (int)(p.tiles * g);
-  hipLaunchKernelGGL(kern, dim3((unsigned)p.total), dim3(kPaWaves * 64), PC::kLdsBytes, stream,
-                     p);
+  hipLaunchKernelGGL(kern, dim3((unsigned)p.total), dim3(W * 64), PC::kLdsBytes, stream, p);
   return hipGetLastError();
 }
 
@@ -1353,11 +1361,11 @@ hipError_t launch_poly_apply(const uint16_t* a, const uint16_t* x, uint16_t* c, 
     case 1:
       return launch_poly_apply_nc<1>(p, sh.g, sh.m, sh.n, stream);
     case 2:
-      return launch_poly_apply_nc<2>(p, sh.g, sh.m, sh.n, stream);
+      return launch_poly_apply_nc<2, 8>(p, sh.g, sh.m, sh.n, stream);
     case 3:
       return launch_poly_apply_nc<3>(p, sh.g, sh.m, sh.n, stream);
     case 6:
-      return launch_poly_apply_nc<6>(p, sh.g, sh.m, sh.n, stream);
+      return launch_poly_apply_nc<6, 8>(p, sh.g, sh.m, sh.n, stream);
     default:
       return hipErrorInvalidValue;
   }

@@ -183,12 +183,12 @@ def test_deterministic_and_batch_invariant(gpu_lib, g, m, n):
                                    (24, 200, 328), (32, 200, 696), (24, 256, 768)])
 def test_fused_poly_apply_matches_stack(gpu_lib, g, m, n):
     """Small wide matrices stepped alone form B inside the apply's launch (one launch per map
-    instead of two, column tiles of one 128-column chunk).  Stacks (44, 200, 328), (66, 136, 136)
-    and (24, 256, 768) run the polynomial and the apply as separate kernels (the first and last
-    with 64x64 polynomial tiles, the last with the Gram's k groups on separate waves of 64x64
-    tiles); the others take the fused launch with column tiles of 2, 3 and 6 chunks (the last
-    column tile ragged where n is not a multiple of the tile).  Each matrix's step must be the
-    same bit for bit either way."""
+    instead of two, column tiles of one 128-column chunk, four waves).  Stacks (44, 200, 328)
+    and (66, 136, 136) run the polynomial and the apply as separate kernels (the first with 64x64
+    polynomial tiles); the others take the fused launch with column tiles of 2 (eight waves), 3
+    (four) and 6 chunks (eight; the last column tile ragged where n is not a multiple of the
+    tile), and (24, 256, 768) runs its Gram's k groups on separate waves of 64x64 tiles.  Each
+    matrix's step must be the same bit for bit either way."""
     import torch
     G = to_gpu_f32(_gauss_steps(g, m, n, 21, 1)[0])
     vs = torch.randn((2, g, m, n), dtype=torch.float32, device="cuda")
