@@ -62,8 +62,12 @@ __host__ __device__ __forceinline__ RailWeights rail_weights(float momentum, flo
 
 // Groups of 4 elements per thread per iteration, and workgroups per CU of the grid (grid-stride
 // beyond); chosen by measurement on MI355X (about 6.7 TB/s on the 24x2816x768 bank, against 5.2
-// with 16 workgroups per CU and cacheable rail loads).
+// with 16 workgroups per CU and cacheable rail loads).  Banks of at most 2^24 elements take one
+// group per thread (more, shorter threads: qk 24.9 -> 22.6 us, vo 54.2 -> 51.6 us); on the
+// larger banks that costs 4-11%.
 constexpr int kUnroll = 4;
+constexpr int kSmallUnroll = 1;
+constexpr int64_t kSmallCount = int64_t(1) << 24;
 constexpr int kBlocksPerCu = 64;
 
 // 4 gradient values as fp32: a 16-byte fp32 load, or an 8-byte bf16 load widened exactly.
@@ -124,19 +128,27 @@ __global__ __launch_bounds__(256) void momentum_kernel(const GradT* __restrict__
   }
 }
 
-template <typename GradT>
-hipError_t launch_momentum_t(const GradT* grad, float* v0, float* v1, uint16_t* x, int64_t count,
+template <int UNROLL, typename GradT>
+hipError_t launch_momentum_u(const GradT* grad, float* v0, float* v1, uint16_t* x, int64_t count,
                              RailWeights rw, const float* scalars, hipStream_t stream) {
   const int64_t n4 = count / 4;
   const int threads = 256;
-  int64_t blocks = (n4 + threads * kUnroll - 1) / (threads * kUnroll);
+  int64_t blocks = (n4 + threads * UNROLL - 1) / (threads * UNROLL);
   const int64_t max_blocks = 256 * kBlocksPerCu;
   if (blocks > max_blocks) blocks = max_blocks;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL((momentum_kernel<kUnroll, GradT>), dim3((unsigned)blocks), dim3(threads), 0,
+  hipLaunchKernelGGL((momentum_kernel<UNROLL, GradT>), dim3((unsigned)blocks), dim3(threads), 0,
                      stream, grad, reinterpret_cast<f32x4_t*>(v0), reinterpret_cast<f32x4_t*>(v1),
                      reinterpret_cast<u32x2_t*>(x), n4, rw, scalars);
   return hipGetLastError();
+}
+
+template <typename GradT>
+hipError_t launch_momentum_t(const GradT* grad, float* v0, float* v1, uint16_t* x, int64_t count,
+                             RailWeights rw, const float* scalars, hipStream_t stream) {
+  if (count <= kSmallCount)
+    return launch_momentum_u<kSmallUnroll>(grad, v0, v1, x, count, rw, scalars, stream);
+  return launch_momentum_u<kUnroll>(grad, v0, v1, x, count, rw, scalars, stream);
 }
 
 }  // namespace
