@@ -121,7 +121,8 @@ int check_disjoint(std::initializer_list<Buf> bufs) {
 int check_step_args(const void* grad, size_t grad_bytes, float* velocity, uint16_t* out,
                     const Shape& sh) {
   if (!grad || !velocity || !out) return ANVIL_ERR_INVALID_ARG;
-  if (!aligned(grad, 16) || !aligned(velocity, 16) || !aligned(out, 16)) return ANVIL_ERR_MISALIGNED;
+  if (!aligned(grad, 16) || !aligned(velocity, 16) || !aligned(out, 16))
+    return ANVIL_ERR_MISALIGNED;
   const size_t cnt = static_cast<size_t>(sh.g) * sh.m * sh.n;
   return check_disjoint({{grad, cnt * grad_bytes}, {velocity, cnt * 8}, {out, cnt * 2}});
 }
@@ -659,7 +660,8 @@ int anvil_normalize(uint16_t* x, uint16_t* a, const float* trace_partials, float
   const size_t s = sh.s();
   const size_t xb = static_cast<size_t>(sh.g) * sh.m * sh.n * 2, ab = sh.g * s * s * 2;
   const size_t tb = static_cast<size_t>(sh.g) * anvil::gram_trace_slots(sh) * 4;
-  if (overlap(x, xb, a, ab) || overlap(x, xb, trace_partials, tb) || overlap(a, ab, trace_partials, tb) ||
+  if (overlap(x, xb, a, ab) || overlap(x, xb, trace_partials, tb) ||
+      overlap(a, ab, trace_partials, tb) ||
       (d_out && (overlap(d_out, sh.g * 4, x, xb) || overlap(d_out, sh.g * 4, a, ab) ||
                  overlap(d_out, sh.g * 4, trace_partials, tb))))
     return ANVIL_ERR_ALIAS;

@@ -279,9 +279,11 @@ __device__ __forceinline__ void upper_tile(int t, int tiles, int* ti, int* tj) {
   *tj = i + t;
 }
 
-// Diagonal tiles of an upper-triangle tile grid (tiles_m tiles per side, tiles = tiles_m(tiles_m+1)/2
-// per matrix, row by row): the diagonal tile of row i sits at t = i*tiles_m - i(i-1)/2.
-__device__ __forceinline__ int diag_pos(int i, int tiles_m) { return i * tiles_m - i * (i - 1) / 2; }
+// Diagonal tiles of an upper-triangle tile grid (tiles_m tiles per side, tiles_m(tiles_m+1)/2 per
+// matrix, row by row): the diagonal tile of row i sits at t = i*tiles_m - i(i-1)/2.
+__device__ __forceinline__ int diag_pos(int i, int tiles_m) {
+  return i * tiles_m - i * (i - 1) / 2;
+}
 
 // Number of diagonal tiles with logical id below L (matrices one after the other).
 __device__ __forceinline__ int diagonals_before(int L, int tiles, int tiles_m) {
@@ -293,12 +295,12 @@ __device__ __forceinline__ int diagonals_before(int L, int tiles, int tiles_m) {
 
 // Gram launches with one to two rounds of workgroups: the first round puts one workgroup on every
 // CU of an XCD (32 per XCD) and each later workgroup of the XCD shares a CU with one of the first
-// (observed: workgroup 32+k of an XCD joins the CU of workgroup k).  A CU
-// holding two workgroups sets the launch's time, so those slots take the XCD's cheaper diagonal
-// tiles (one operand copy, a wave fewer multiplying) first: workgroup `local` of an XCD whose
-// logical range is [start, start + count) gets the rank-th tile of the range in diagonal-first
-// order, where the shared slots (0..p-1 and 32..count-1, p = count - 32) come first.  The result
-// is a permutation of the range; which tile a workgroup takes changes no arithmetic.
+// (observed: workgroup 32+k of an XCD joins the CU of workgroup k).  A CU holding two workgroups
+// sets the launch's time, so those slots take the XCD's cheaper diagonal tiles (one operand copy,
+// a wave fewer multiplying) first: workgroup `local` of an XCD whose logical range is
+// [start, start + count) gets the rank-th tile of the range in diagonal-first order, where the
+// shared slots (0..p-1 and 32..count-1, p = count - 32) come first.  The result is a permutation
+// of the range; which tile a workgroup takes changes no arithmetic.
 __device__ __forceinline__ int diagonal_first(int start, int count, int local, int tiles,
                                               int tiles_m) {
   constexpr int kCusPerXcd = 32;

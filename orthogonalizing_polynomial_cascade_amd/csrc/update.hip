@@ -9,7 +9,8 @@
 // longer one.  Per matrix, in fp32:
 //   power[l] = mean over the lane of u^2             pre  = sqrt(sum_l power[l] * len)
 //   e[l]     = lerp(e[l], power[l], 1 - beta2)        gain = 1 / sqrt(max(e[l], 1e-10))
-//   post     = sqrt(sum_l (power[l] * len) * gain^2)  scale[l] = bf16(gain * (pre / max(post, 1e-10)))
+//   post     = sqrt(sum_l (power[l] * len) * gain^2)
+//   scale[l] = bf16(gain * (pre / max(post, 1e-10)))
 //   u       <- bf16(u * scale[lane])
 // then, per element, with the fp32 master m = (param bits << 16) | mantissa:
 //   m <- (m - ((m * [gate * m >= 0]) * wd) * lr[matrix]) - u * lr[matrix]
