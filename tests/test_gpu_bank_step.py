@@ -155,13 +155,14 @@ def test_full_size_history(gpu_lib, wname):
     assert len(rows) == len(check) * len(sample)
 
 
-@pytest.mark.parametrize("g,m,n", [(4, 392, 136), (4, 2816, 768), (44, 392, 264), (44, 264, 392)])
+@pytest.mark.parametrize("g,m,n", [(4, 392, 136), (4, 2816, 768), (44, 392, 264), (44, 264, 392),
+                                   (300, 8, 72), (300, 72, 8)])
 def test_deterministic_and_batch_invariant(gpu_lib, g, m, n):
     """Repeated calls agree bit for bit, and so does each matrix stepped alone.  For 4x2816x768
     the stack's apply runs 128x256 tiles and a single matrix's 128x128 tiles: the tile shape must
     not change any element's arithmetic.  The 44-matrix stacks have 264 Gram tiles, 132 of them
     diagonal, so their Gram hands the CU-sharing workgroup slots to diagonal tiles (a different
-    tile order from a single matrix's)."""
+    tile order from a single matrix's); so do the 300-matrix stacks of one-tile Grams."""
     import torch
     G = to_gpu_f32(_gauss_steps(g, m, n, 5, 1)[0])
     v0 = torch.randn((2, g, m, n), dtype=torch.float32, device="cuda")
