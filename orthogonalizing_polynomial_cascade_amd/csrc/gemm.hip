@@ -17,6 +17,9 @@
 //          wide: C = a X + B X   (P = B, Q(j, k) = X[k][j]: K-major)
 //          epilogue bf16(a * X[i][j] + acc), or with split rounding
 //          bf16(bf16(acc) + a * X[i][j]) (the page's two-kernel form for banks of > 1024 rows).
+//          The tall apply's X[i][j] is its own P operand at k = j: each wave keeps the MFMA
+//          fragments of X that cover its columns as the k loop passes them, and its epilogue
+//          loads nothing from memory.
 //
 // The Gram and the polynomial are symmetric: only tiles on or above the diagonal are computed,
 // and each is stored twice (C[i][j] and C[j][i]) from the same fp32 value, so the stored matrices
@@ -73,7 +76,10 @@ namespace anvil {
 
 namespace {
 
-enum { OP_GRAM = 0, OP_POLY = 1, OP_APPLY = 2 };
+// OP_APPLY_XT: the tall apply (C = a X + X B), whose epilogue operand X[i][j] is its own P
+// operand at k = j (see the stash in gemm_kernel).
+enum { OP_GRAM = 0, OP_POLY = 1, OP_APPLY = 2, OP_APPLY_XT = 3 };
+
 
 constexpr uint32_t kOOB = 0x80000000u;   // buffer offset past any range: the load returns 0
 constexpr int kCus = 256;                // compute units of the MI355X (8 XCDs of 32)
@@ -349,8 +355,12 @@ struct Cfg {
 
 // The four-wave Gram tiles run two workgroups per CU, two waves per SIMD: they may take up to 256
 // registers per lane, which their read-ahead of a whole slab's fragments needs.
+// The eight-wave tall apply keeps four waves per SIMD (two workgroups per CU) with its kept X
+// fragments: 128 registers.
 template <int OP, int WAVES, int KSPLIT>
-constexpr int kMinWavesPerEu = OP == OP_GRAM && WAVES == 4 && KSPLIT == 1 ? 2 : 1;
+constexpr int kMinWavesPerEu = OP == OP_GRAM && WAVES == 4 && KSPLIT == 1 ? 2
+                               : OP == OP_APPLY_XT && WAVES == 8      ? 4
+                                                                      : 1;
 
 // KSPLIT > 1 (Gram tiles with slab groups only): the tile's KSPLIT slab groups go to KSPLIT sets
 // of WM x WN waves, each set with its own ring, which accumulate one group each from zero; the
@@ -365,6 +375,7 @@ __global__ __launch_bounds__(WM * WN * KSPLIT * 64)
 __attribute__((amdgpu_waves_per_eu(kMinWavesPerEu<OP, WM * WN, KSPLIT>)))
 void gemm_kernel(GemmParams p) {
   using C = Cfg<BM, BN, WM, WN, STAGES, BK>;
+  constexpr bool kApply = OP == OP_APPLY || OP == OP_APPLY_XT;
   static_assert(KSPLIT == 1 || (OP == OP_GRAM && SLAB > 0 && STAGES == 2),
                 "k groups over waves: Gram tiles with slab groups and two stages");
   static_assert(KSPLIT == 1 || C::kWaves == 1 || (WM == WN && C::kWTM == 32 && C::kWTN == 32),
@@ -393,7 +404,7 @@ void gemm_kernel(GemmParams p) {
   const int64_t b = logical / p.tiles;
   const int t = logical % p.tiles;
   int ti, tj;
-  if constexpr (OP == OP_APPLY) {
+  if constexpr (kApply) {
     ti = t / p.tiles_n;
     tj = t % p.tiles_n;
   } else {
@@ -410,7 +421,7 @@ void gemm_kernel(GemmParams p) {
   // A diagonal tile of a symmetric product has the same rows in both operands: it copies them once
   // and reads both operands' fragments from that slab (with two stages every slab iteration waits
   // for all of this wave's copies, so the copy count does not enter the waits).
-  const bool same_pq = STAGES == 2 && PT == QT && BM == BN && OP != OP_APPLY && ti == tj;
+  const bool same_pq = STAGES == 2 && PT == QT && BM == BN && !kApply && ti == tj;
 
   f32x16_t acc[C::kFM][C::kFN];
 #pragma unroll
@@ -440,7 +451,22 @@ void gemm_kernel(GemmParams p) {
   constexpr int kLanesPerRow = C::kWTN / 8;
   constexpr int kRowsPerPass = 64 / kLanesPerRow;
   constexpr int kPasses = 32 / kRowsPerPass;
-  constexpr bool kHasE = OP != OP_GRAM;
+  // Tall apply: X[i][j] of this wave's block is its P operand at k = j, and it passes through the
+  // wave's registers as MFMA fragments while the k loop crosses the wave's columns (k-steps
+  // xs0 .. xs0 + kXsKs - 1).  Those fragments of its kXsFm 32-row blocks (all of them) are kept,
+  // 32 registers for a 64x64 wave block, and the epilogue takes X from them instead of reading it
+  // again from memory (by then it has left L2: one mlp apply re-read ~90 MB of it from HBM).
+  constexpr int kXsFm = OP == OP_APPLY_XT ? C::kFM : 0;
+  constexpr int kXsKs = C::kWTN / 16;
+  const int xs0 = (j0 + wn * C::kWTN) / 16;
+  bf16x8_t xs[kXsFm > 0 ? kXsKs : 1][kXsFm > 0 ? kXsFm : 1];
+  if constexpr (kXsFm > 0) {
+#pragma unroll
+    for (int q = 0; q < kXsKs; ++q)
+#pragma unroll
+      for (int fm = 0; fm < kXsFm; ++fm) xs[q][fm] = bf16x8_t{};
+  }
+  constexpr bool kHasE = OP != OP_GRAM && kXsFm < C::kFM;   // some blocks read E from memory
   const uint16_t* Eb = p.E ? p.E + b * p.strideE : nullptr;
   u32x4_t ecur[kHasE ? kPasses : 1];
   auto load_e = [&](u32x4_t* dst, int fm) {
@@ -457,7 +483,7 @@ void gemm_kernel(GemmParams p) {
   // On a diagonal tile of a symmetric product, a wave whose block lies wholly below the diagonal
   // stores nothing (those entries come from the mirror of the block above it): it takes its share
   // of the copies and every barrier, but skips its fragment reads and multiplies.
-  const bool idle = (OP != OP_APPLY) && ti == tj && wm * C::kWTM >= (wn + 1) * C::kWTN;
+  const bool idle = !kApply && ti == tj && wm * C::kWTM >= (wn + 1) * C::kWTN;
 
   f32x16_t slab[SLAB > 0 ? C::kFM : 1][SLAB > 0 ? C::kFN : 1];
   constexpr bool kPadded = KSPLIT > 1 && C::kWaves > 1;   // uniform trip count: shared barriers
@@ -486,7 +512,7 @@ void gemm_kernel(GemmParams p) {
     }
     if (kPadded && kt >= KT) continue;
     if constexpr (kHasE) {
-      if (kt == KT - 1) load_e(ecur, 0);
+      if (kt == KT - 1) load_e(ecur, kXsFm);
     }
     if (idle) continue;
     const char* tp = smem + ((kt - kt0) % STAGES) * C::kStageBytes;
@@ -531,6 +557,17 @@ void gemm_kernel(GemmParams p) {
         }
         // keep the reads ahead of the multiplies (the scheduler would sink each to its use)
         if constexpr (kHoist) __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (kXsFm > 0) {
+        const int aks = kt * kKs + ks;
+#pragma unroll
+        for (int q = 0; q < kXsKs; ++q)
+          if (aks == xs0 + q) {
+            // a real branch (taken on a few slabs): keeps the copies out of the other slabs
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int fm = 0; fm < kXsFm; ++fm) xs[q][fm] = fa[ks][fm];
+          }
       }
 #pragma unroll
       for (int fm = 0; fm < C::kFM; ++fm)
@@ -608,7 +645,7 @@ void gemm_kernel(GemmParams p) {
     return epi + row * C::kEpiPitch + (col ^ (row & 16));
   };
   uint16_t* Cb = p.C + b * p.strideC;
-  const bool diag_tile = (OP != OP_APPLY) && ti == tj;
+  const bool diag_tile = !kApply && ti == tj;
   float tsum = 0.0f;
 
 #pragma unroll
@@ -616,7 +653,23 @@ void gemm_kernel(GemmParams p) {
     if (!computes) break;
     u32x4_t enext[kHasE ? kPasses : 1];
     if constexpr (kHasE) {
-      if (fm + 1 < C::kFM) load_e(enext, fm + 1);
+      if (fm + 1 < C::kFM && fm + 1 > kXsFm) load_e(enext, fm + 1);
+    }
+    // A kept block's X: lane l holds row l%32 at k = 16q + 8(l/32) + 0..7 of k-step q, while its
+    // accumulator holds columns 8q' + 4(l/32) + 0..3 of each 32-column fragment.  Swapping dwords
+    // 2, 3 of the lower 32 lanes with dwords 0, 1 of the upper 32 leaves every lane with its own
+    // columns: dwords 0, 1 of k-step 2fn + q'/2 for even q', dwords 2, 3 for odd q'.
+    u32x4_t xw[kXsFm > 0 ? kXsKs : 1];
+    if constexpr (kXsFm > 0) {
+      if (fm < kXsFm) {
+#pragma unroll
+        for (int q = 0; q < kXsKs; ++q) {
+          const u32x4_t w = __builtin_bit_cast(u32x4_t, xs[q][fm]);
+          const auto s02 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+          const auto s13 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+          xw[q] = u32x4_t{s02[0], s13[0], s02[1], s13[1]};
+        }
+      }
     }
 #pragma unroll
     for (int fn = 0; fn < C::kFN; ++fn)
@@ -624,9 +677,21 @@ void gemm_kernel(GemmParams p) {
       for (int q = 0; q < 4; ++q) {
         const int row = lane & 31;
         const int col = fn * 32 + 8 * q + 4 * (lane >> 5);
-        *reinterpret_cast<f32x4_t*>(ep(row, col)) =
-            f32x4_t{acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1], acc[fm][fn][4 * q + 2],
-                    acc[fm][fn][4 * q + 3]};
+        float v[4] = {acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1], acc[fm][fn][4 * q + 2],
+                      acc[fm][fn][4 * q + 3]};
+        if constexpr (kXsFm > 0) {
+          if (fm < kXsFm) {
+            // the apply's epilogue expression, as in the direct pass below
+            const u32x4_t w = xw[2 * fn + q / 2];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t d = w[2 * (q % 2) + e / 2];
+              const float ax = p.alpha * bf16_to_f32((e % 2) ? (d >> 16) : (d & 0xFFFFu));
+              v[e] = p.split ? bf16_to_f32(f32_to_bf16(v[e])) + ax : ax + v[e];
+            }
+          }
+        }
+        *reinterpret_cast<f32x4_t*>(ep(row, col)) = f32x4_t{v[0], v[1], v[2], v[3]};
       }
     wait_lds();
     __builtin_amdgcn_wave_barrier();
@@ -675,8 +740,15 @@ void gemm_kernel(GemmParams p) {
       const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(ep(row, col + 4));
       float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
       u32x4_t out;
-      if constexpr (OP == OP_APPLY) {
-        const u32x4_t xe = ecur[pass];
+      if constexpr (kApply) {
+        if (fm < kXsFm) {
+          // a kept block is already a·X + P (or its split form) in fp32
+#pragma unroll
+          for (int e = 0; e < 4; ++e) out[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
+          *reinterpret_cast<u32x4_t*>(Cb + (int64_t)gi * p.ldc + gj) = out;
+          continue;
+        }
+        const u32x4_t xe = ecur[kHasE ? pass : 0];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float ax0 = p.alpha * bf16_to_f32(xe[e] & 0xFFFFu);
@@ -726,7 +798,7 @@ void gemm_kernel(GemmParams p) {
       }
     }
 
-    if constexpr (OP != OP_APPLY) {
+    if constexpr (!kApply) {
       wait_lds();
       __builtin_amdgcn_wave_barrier();
       // mirror: C[gj][gi .. gi+7] from LDS column gj, rows gi .. gi+7 (8-row groups); lanes
@@ -754,7 +826,7 @@ void gemm_kernel(GemmParams p) {
     wait_lds();
     __builtin_amdgcn_wave_barrier();
     if constexpr (kHasE) {
-      if (fm + 1 < C::kFM) {
+      if (fm + 1 < C::kFM && fm + 1 > kXsFm) {
 #pragma unroll
         for (int pass = 0; pass < kPasses; ++pass) ecur[pass] = enext[pass];
       }
@@ -1259,7 +1331,7 @@ hipError_t launch_apply_cfg(const uint16_t* x, const uint16_t* bm, uint16_t* c, 
     p.bytesQ = (uint32_t)((int64_t)s * s * 2);
     p.ldq = s;
     p.K = sh.n;
-    return launch<OP_APPLY, false, true, BM, BN, WM, WN, STAGES, BK, 0>(p, sh.g, stream);
+    return launch<OP_APPLY_XT, false, true, BM, BN, WM, WN, STAGES, BK, 0>(p, sh.g, stream);
   }
   // C = a X + B X: P = rows of B (K = m contiguous), Q(j, k) = X[k][j] (K-major)
   p.P = bm;
