@@ -76,8 +76,9 @@ namespace anvil {
 
 namespace {
 
+// OP_APPLY: the wide apply (C = a X + B X), which reads its epilogue operand X[i][j] from memory.
 // OP_APPLY_XT: the tall apply (C = a X + X B), whose epilogue operand X[i][j] is its own P
-// operand at k = j (see the stash in gemm_kernel).
+// operand at k = j (kept from the k loop, see gemm_kernel).
 enum { OP_GRAM = 0, OP_POLY = 1, OP_APPLY = 2, OP_APPLY_XT = 3 };
 
 
@@ -182,48 +183,69 @@ template <bool KMAJOR, int ROWS, int BK, int NW>
 struct SlabCopy {
   static constexpr int kInsts = ROWS * BK / 512 / NW;
   static_assert(ROWS * BK / 512 % NW == 0, "slab instructions must split evenly over the waves");
-  uint32_t vbase[kInsts];   // byte offset at k0 = 0, or kOOB for rows past the edge
-  int kin[kInsts];          // the lane's k offset inside the slab (for the ragged last slab)
-  uint32_t kbytes;          // bytes per unit of k0
+  // K-major: a wave's instructions i = 0, 1, .. cover k-rows kStepRows apart; when that keeps the
+  // slot swizzle (k-row & 3), every instruction reads the same columns, so its offset is the
+  // first one's plus i * kStepRows rows (past-the-edge lanes stay past the range), one register.
+  static constexpr int kStepRows = KMAJOR ? NW * (512 / ROWS) : 0;
+  static constexpr bool kOneBase = KMAJOR && kStepRows % 4 == 0;
+  uint32_t vbase[kOneBase ? 1 : kInsts];   // byte offset at k0 = 0, or kOOB past the edge
+  uint32_t kbytes;                         // bytes per unit of k0
+
+  // Row (K-contiguous: row of the slab; K-major: k-row) and 16-byte slot of lane `lane`'s piece
+  // in instruction i.
+  __device__ static __forceinline__ void piece(int i, int wave, int lane, int* row, int* c) {
+    const int u = wave + i * NW;
+    if constexpr (!KMAJOR) {
+      constexpr int kSlots = BK / 8;
+      constexpr int kRowsPerInst = 64 / kSlots;
+      *row = kRowsPerInst * u + lane / kSlots;
+      *c = (lane % kSlots) ^ KContig<ROWS, BK>::swz(*row);
+    } else {
+      constexpr int kSlots = ROWS / 8;
+      constexpr int kRowsPerKb = 64 / kSlots;
+      *row = u * kRowsPerKb + lane / kSlots;
+      *c = (lane % kSlots) ^ ((*row & 3) << 2);
+    }
+  }
 
   SlabCopy() = default;
   __device__ __forceinline__ SlabCopy(int ld, int row0, int rows, int wave, int lane) {
     kbytes = KMAJOR ? 2u * (uint32_t)ld : 2u;
 #pragma unroll
-    for (int i = 0; i < kInsts; ++i) {
-      const int u = wave + i * NW;
+    for (int i = 0; i < (kOneBase ? 1 : kInsts); ++i) {
+      int row, c;
+      piece(i, wave, lane, &row, &c);
       if constexpr (!KMAJOR) {
-        constexpr int kSlots = BK / 8;
-        constexpr int kRowsPerInst = 64 / kSlots;
-        const int row = kRowsPerInst * u + lane / kSlots;
-        const int c = (lane % kSlots) ^ KContig<ROWS, BK>::swz(row);
         const int gr = row0 + row;
-        kin[i] = c * 8;
         vbase[i] = gr < rows ? (uint32_t)(gr * ld + c * 8) * 2u : kOOB;
       } else {
-        constexpr int kSlots = ROWS / 8;
-        constexpr int kRowsPerKb = 64 / kSlots;
-        const int kr = u * kRowsPerKb + lane / kSlots;
-        const int c = (lane % kSlots) ^ ((kr & 3) << 2);
         const int gr = row0 + c * 8;
-        kin[i] = kr;
-        vbase[i] = gr < rows ? (uint32_t)(kr * ld + gr) * 2u : kOOB;
+        vbase[i] = gr < rows ? (uint32_t)(row * ld + gr) * 2u : kOOB;
       }
     }
   }
 
   // Issue this wave's instructions of the slab at k0 into LDS at byte address `dst` (uniform).
+  // The lane's k offset inside a ragged last slab is recomputed there (not kept in registers).
   __device__ __forceinline__ void issue(i32x4_t rsrc, uint32_t dst, int k0, int K, int wave) const {
     const uint32_t koff = (uint32_t)k0 * kbytes;
+    auto base = [&](int i) {
+      return kOneBase ? vbase[0] + (uint32_t)(i * kStepRows) * kbytes : vbase[kOneBase ? 0 : i];
+    };
     if (k0 + BK <= K) {
 #pragma unroll
       for (int i = 0; i < kInsts; ++i)
-        dma16(rsrc, dst + (uint32_t)(wave + i * NW) * 1024u, vbase[i] + koff);
+        dma16(rsrc, dst + (uint32_t)(wave + i * NW) * 1024u, base(i) + koff);
     } else {
+      const int lane = __lane_id();
 #pragma unroll
-      for (int i = 0; i < kInsts; ++i)
+      for (int i = 0; i < kInsts; ++i) {
+        int row, c;
+        piece(i, wave, lane, &row, &c);
+        const int kin = KMAJOR ? row : c * 8;
         dma16(rsrc, dst + (uint32_t)(wave + i * NW) * 1024u,
-              k0 + kin[i] < K ? vbase[i] + koff : kOOB);
+              k0 + kin < K ? base(i) + koff : kOOB);
+      }
     }
   }
 };
@@ -698,6 +720,7 @@ void gemm_kernel(GemmParams p) {
 
     const int gi0 = i0 + wm * C::kWTM + fm * 32;   // first global row of this block
     const int gj0 = j0 + wn * C::kWTN;             // first global col of this wave
+
 
     if constexpr (OP == OP_POLY) {
       // B = b*A + c*(A*A): every piece of the block is combined in LDS first, so that the
@@ -1300,40 +1323,46 @@ hipError_t launch_poly(const uint16_t* a, uint16_t* bout, float coef_b, float co
   return launch<OP_POLY, false, false, 128, 128, 2, 4, 2, 64, 0>(p, g, stream);
 }
 
+// Tall apply, C = a X + X B: P = X rows (K = n contiguous); Q(j, k) = B[k][j] (K-major: B is
+// symmetric, and a slab of its rows k is 2*BN contiguous bytes per row where the K-contiguous form
+// would fetch 2*BK-byte pieces, half a cache line at BK = 32; measured 1.3% faster per mlp step).
 template <int BM, int BN, int WM, int WN, int STAGES, int BK>
-hipError_t launch_apply_cfg(const uint16_t* x, const uint16_t* bm, uint16_t* c, float coef_a,
-                            bool split, const Shape& sh, hipStream_t stream) {
+hipError_t launch_apply_tall(const uint16_t* x, const uint16_t* bm, uint16_t* c, float coef_a,
+                             bool split, const Shape& sh, hipStream_t stream) {
   const int s = sh.s();
   GemmParams p{};
   p.M = sh.m;
   p.N = sh.n;
+  p.K = sh.n;
+  p.P = x;
+  p.strideP = (int64_t)sh.m * sh.n;
+  p.bytesP = (uint32_t)((int64_t)sh.m * sh.n * 2);
+  p.ldp = sh.n;
+  p.Q = bm;
+  p.strideQ = (int64_t)s * s;
+  p.bytesQ = (uint32_t)((int64_t)s * s * 2);
+  p.ldq = s;
   p.C = c;
   p.strideC = (int64_t)sh.m * sh.n;
   p.ldc = sh.n;
-  p.E = x;
-  p.strideE = (int64_t)sh.m * sh.n;
-  p.lde = sh.n;
   p.alpha = coef_a;
   p.split = split ? 1 : 0;
-  p.tiles_m = ceil_div(sh.m, BM);
-  p.tiles_n = ceil_div(sh.n, BN);
+  p.tiles_m = ceil_div(p.M, BM);
+  p.tiles_n = ceil_div(p.N, BN);
   p.tiles = p.tiles_m * p.tiles_n;
-  if (sh.tall()) {
-    // C = a X + X B: P = X rows (K = n contiguous); Q(j, k) = B[k][j] (K-major: B is symmetric,
-    // and a slab of its rows k is 2*BN contiguous bytes per row where the K-contiguous form would
-    // fetch 2*BK-byte pieces, half a cache line at BK = 32; measured 1.3% faster per mlp step)
-    p.P = x;
-    p.strideP = (int64_t)sh.m * sh.n;
-    p.bytesP = (uint32_t)((int64_t)sh.m * sh.n * 2);
-    p.ldp = sh.n;
-    p.Q = bm;
-    p.strideQ = (int64_t)s * s;
-    p.bytesQ = (uint32_t)((int64_t)s * s * 2);
-    p.ldq = s;
-    p.K = sh.n;
-    return launch<OP_APPLY_XT, false, true, BM, BN, WM, WN, STAGES, BK, 0>(p, sh.g, stream);
-  }
-  // C = a X + B X: P = rows of B (K = m contiguous), Q(j, k) = X[k][j] (K-major)
+  return launch<OP_APPLY_XT, false, true, BM, BN, WM, WN, STAGES, BK, 0>(p, sh.g, stream);
+}
+
+// Wide (and square) apply, C = a X + B X: P = rows of B (K = m contiguous), Q(j, k) = X[k][j]
+// (K-major); the epilogue reads a X[i][j] from memory.
+template <int BM, int BN, int WM, int WN, int STAGES, int BK>
+hipError_t launch_apply_wide(const uint16_t* x, const uint16_t* bm, uint16_t* c, float coef_a,
+                             bool split, const Shape& sh, hipStream_t stream) {
+  const int s = sh.s();
+  GemmParams p{};
+  p.M = sh.m;
+  p.N = sh.n;
+  p.K = sh.m;
   p.P = bm;
   p.strideP = (int64_t)s * s;
   p.bytesP = (uint32_t)((int64_t)s * s * 2);
@@ -1342,7 +1371,17 @@ hipError_t launch_apply_cfg(const uint16_t* x, const uint16_t* bm, uint16_t* c, 
   p.strideQ = (int64_t)sh.m * sh.n;
   p.bytesQ = (uint32_t)((int64_t)sh.m * sh.n * 2);
   p.ldq = sh.n;
-  p.K = sh.m;
+  p.C = c;
+  p.strideC = (int64_t)sh.m * sh.n;
+  p.ldc = sh.n;
+  p.E = x;
+  p.strideE = (int64_t)sh.m * sh.n;
+  p.lde = sh.n;
+  p.alpha = coef_a;
+  p.split = split ? 1 : 0;
+  p.tiles_m = ceil_div(p.M, BM);
+  p.tiles_n = ceil_div(p.N, BN);
+  p.tiles = p.tiles_m * p.tiles_n;
   return launch<OP_APPLY, false, true, BM, BN, WM, WN, STAGES, BK, 0>(p, sh.g, stream);
 }
 
@@ -1362,13 +1401,23 @@ ApplyTiles apply_tiles(const Shape& sh) {
 
 hipError_t launch_apply(const uint16_t* x, const uint16_t* bm, uint16_t* c, float coef_a,
                         bool split, const Shape& sh, hipStream_t stream) {
+  if (sh.tall()) {
+    switch (apply_tiles(sh)) {
+      case kApply128x256:
+        return launch_apply_tall<128, 256, 2, 4, 2, 32>(x, bm, c, coef_a, split, sh, stream);
+      case kApply32x128:
+        return launch_apply_tall<32, 128, 1, 2, 2, 64>(x, bm, c, coef_a, split, sh, stream);
+      default:
+        return launch_apply_tall<128, 128, 2, 4, 2, 64>(x, bm, c, coef_a, split, sh, stream);
+    }
+  }
   switch (apply_tiles(sh)) {
     case kApply128x256:
-      return launch_apply_cfg<128, 256, 2, 4, 2, 32>(x, bm, c, coef_a, split, sh, stream);
+      return launch_apply_wide<128, 256, 2, 4, 2, 32>(x, bm, c, coef_a, split, sh, stream);
     case kApply32x128:
-      return launch_apply_cfg<32, 128, 1, 2, 2, 64>(x, bm, c, coef_a, split, sh, stream);
+      return launch_apply_wide<32, 128, 1, 2, 2, 64>(x, bm, c, coef_a, split, sh, stream);
     default:
-      return launch_apply_cfg<128, 128, 2, 4, 2, 64>(x, bm, c, coef_a, split, sh, stream);
+      return launch_apply_wide<128, 128, 2, 4, 2, 64>(x, bm, c, coef_a, split, sh, stream);
   }
 }
 
