@@ -565,7 +565,7 @@ def main():
         "poly_tflops": rec["poly_in_step_tflops"],
         "apply_tflops": rec["apply_in_step_tflops"],
         "stage_loop_tflops": {k: rec[f"{k}_tflops"] for k in ("gram", "poly", "apply")},
-        "roofline": {"bound": "mfma", "kernel": "apply (gemm_kernel<2>)", "achieved": achieved,
+        "roofline": {"bound": "mfma", "kernel": "tall apply (gemm_kernel<3>)", "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "achieved_in_step": achieved_in_step,
                      "frac_in_step": achieved_in_step / PEAK_BF16_TFLOPS,
