@@ -377,12 +377,12 @@ struct Cfg {
 
 // The four-wave Gram tiles run two workgroups per CU, two waves per SIMD: they may take up to 256
 // registers per lane, which their read-ahead of a whole slab's fragments needs.
-// The eight-wave tall apply keeps four waves per SIMD (two workgroups per CU) with its kept X
-// fragments: 128 registers.
+// The eight-wave tall apply and polynomial keep four waves per SIMD (two workgroups per CU) with
+// their kept operand fragments: at most 128 registers.
 template <int OP, int WAVES, int KSPLIT>
 constexpr int kMinWavesPerEu = OP == OP_GRAM && WAVES == 4 && KSPLIT == 1 ? 2
-                               : OP == OP_APPLY_XT && WAVES == 8      ? 4
-                                                                      : 1;
+                               : (OP == OP_APPLY_XT || OP == OP_POLY) && WAVES == 8 ? 4
+                                                                                    : 1;
 
 // KSPLIT > 1 (Gram tiles with slab groups only): the tile's KSPLIT slab groups go to KSPLIT sets
 // of WM x WN waves, each set with its own ring, which accumulate one group each from zero; the
@@ -473,12 +473,13 @@ void gemm_kernel(GemmParams p) {
   constexpr int kLanesPerRow = C::kWTN / 8;
   constexpr int kRowsPerPass = 64 / kLanesPerRow;
   constexpr int kPasses = 32 / kRowsPerPass;
-  // Tall apply: X[i][j] of this wave's block is its P operand at k = j, and it passes through the
-  // wave's registers as MFMA fragments while the k loop crosses the wave's columns (k-steps
-  // xs0 .. xs0 + kXsKs - 1).  Those fragments of its kXsFm 32-row blocks (all of them) are kept,
-  // 32 registers for a 64x64 wave block, and the epilogue takes X from them instead of reading it
-  // again from memory (by then it has left L2: one mlp apply re-read ~90 MB of it from HBM).
-  constexpr int kXsFm = OP == OP_APPLY_XT ? C::kFM : 0;
+  // Tall apply and polynomial: the epilogue operand (X[i][j], A[i][j]) of this wave's block is its
+  // P operand at k = j, and it passes through the wave's registers as MFMA fragments while the k
+  // loop crosses the wave's columns (k-steps xs0 .. xs0 + kXsKs - 1).  Those fragments of its
+  // kXsFm 32-row blocks (all of them) are kept, 32 registers for a 64x64 wave block, and the
+  // epilogue takes the operand from them instead of reading it again from memory (for the apply
+  // X has left L2 by then: one mlp apply re-read ~90 MB of it from HBM).
+  constexpr int kXsFm = (OP == OP_APPLY_XT || OP == OP_POLY) ? C::kFM : 0;
   constexpr int kXsKs = C::kWTN / 16;
   const int xs0 = (j0 + wn * C::kWTN) / 16;
   bf16x8_t xs[kXsFm > 0 ? kXsKs : 1][kXsFm > 0 ? kXsFm : 1];
@@ -703,13 +704,18 @@ void gemm_kernel(GemmParams p) {
                       acc[fm][fn][4 * q + 3]};
         if constexpr (kXsFm > 0) {
           if (fm < kXsFm) {
-            // the apply's epilogue expression, as in the direct pass below
+            // the epilogue expressions of the direct pass and of the polynomial's combine below
             const u32x4_t w = xw[2 * fn + q / 2];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const uint32_t d = w[2 * (q % 2) + e / 2];
               const float ax = p.alpha * bf16_to_f32((e % 2) ? (d >> 16) : (d & 0xFFFFu));
-              v[e] = p.split ? bf16_to_f32(f32_to_bf16(v[e])) + ax : ax + v[e];
+              if constexpr (OP == OP_POLY) {
+                const float cq = p.beta * v[e];
+                v[e] = ax + cq;
+              } else {
+                v[e] = p.split ? bf16_to_f32(f32_to_bf16(v[e])) + ax : ax + v[e];
+              }
             }
           }
         }
@@ -722,12 +728,12 @@ void gemm_kernel(GemmParams p) {
     const int gj0 = j0 + wn * C::kWTN;             // first global col of this wave
 
 
-    if constexpr (OP == OP_POLY) {
-      // B = b*A + c*(A*A): every piece of the block is combined in LDS first, so that the
-      // stores below (a diagonal tile's transposed reads and the mirror included) read
-      // finished values
+    if constexpr (OP == OP_POLY && kHasE) {
+      // B = b*A + c*(A*A) for a block without kept A: every piece of the block is combined in LDS
+      // first, so that the stores below (a diagonal tile's transposed reads and the mirror
+      // included) read finished values
 #pragma unroll
-      for (int pass = 0; pass < kPasses; ++pass) {
+      for (int pass = 0; pass < (fm < kXsFm ? 0 : kPasses); ++pass) {
         const int row = pass * kRowsPerPass + lane / kLanesPerRow;
         const int col = (lane % kLanesPerRow) * 8;
         if (gi0 + row >= p.M || gj0 + col >= p.N) continue;
