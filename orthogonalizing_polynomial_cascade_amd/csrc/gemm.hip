@@ -76,9 +76,9 @@ namespace anvil {
 
 namespace {
 
-// OP_APPLY: the wide apply (C = a X + B X), which reads its epilogue operand X[i][j] from memory.
-// OP_APPLY_XT: the tall apply (C = a X + X B), whose epilogue operand X[i][j] is its own P
-// operand at k = j (kept from the k loop, see gemm_kernel).
+// OP_APPLY: the wide apply (C = a X + B X), whose epilogue operand X[i][j] is its Q operand at
+// k = i.  OP_APPLY_XT: the tall apply (C = a X + X B), whose epilogue operand is its P operand at
+// k = j.  Both keep it from the k loop (see gemm_kernel).
 enum { OP_GRAM = 0, OP_POLY = 1, OP_APPLY = 2, OP_APPLY_XT = 3 };
 
 
@@ -102,9 +102,6 @@ struct GemmParams {
   uint16_t* C;
   int64_t strideC;
   int ldc;
-  const uint16_t* E;          // epilogue operand: A (poly) or X (apply)
-  int64_t strideE;
-  int lde;
   float alpha;                // poly: b; apply: a
   float beta;                 // poly: c
   float* trace;               // Gram: per-matrix diagonal partials, or nullptr
@@ -377,12 +374,12 @@ struct Cfg {
 
 // The four-wave Gram tiles run two workgroups per CU, two waves per SIMD: they may take up to 256
 // registers per lane, which their read-ahead of a whole slab's fragments needs.
-// The eight-wave tall apply and polynomial keep four waves per SIMD (two workgroups per CU) with
+// The eight-wave applies and polynomial keep four waves per SIMD (two workgroups per CU) with
 // their kept operand fragments: at most 128 registers.
 template <int OP, int WAVES, int KSPLIT>
 constexpr int kMinWavesPerEu = OP == OP_GRAM && WAVES == 4 && KSPLIT == 1 ? 2
-                               : (OP == OP_APPLY_XT || OP == OP_POLY) && WAVES == 8 ? 4
-                                                                                    : 1;
+                               : OP != OP_GRAM && WAVES == 8         ? 4
+                                                                      : 1;
 
 // KSPLIT > 1 (Gram tiles with slab groups only): the tile's KSPLIT slab groups go to KSPLIT sets
 // of WM x WN waves, each set with its own ring, which accumulate one group each from zero; the
@@ -467,41 +464,30 @@ void gemm_kernel(GemmParams p) {
     }
   }
 
-  // Epilogue operand (X for the apply, A for the polynomial), fetched one 32-row block ahead of
-  // its use (the first block during the last slab) so that the load latency overlaps other work.
-  // Lane mapping as in the epilogue's direct pass: 8 consecutive columns of one row.
-  constexpr int kLanesPerRow = C::kWTN / 8;
+  // Epilogue operand (X for the apply, A for the polynomial).  Tall apply and polynomial: the
+  // operand (X[i][j], A[i][j]) of this wave's block is its P operand at k = j, and it passes
+  // through the wave's registers as MFMA fragments while the k loop crosses the wave's columns
+  // (k-steps xs0 .. xs0 + kXsKs - 1).  The wide apply (C = a X + B X) finds X[i][j] in its Q
+  // operand at k = i, over the k-steps of the wave's rows, transposed (lane l: column j = l%32 of
+  // a 32-column fragment, rows 8(l/32) .. +7 of the k-step).  Those fragments are kept (32
+  // registers for a 64x64 wave block), and the epilogue takes the operand from them instead of
+  // reading it again from memory (for the apply X has left L2 by then: one mlp apply re-read
+  // ~90 MB of it from HBM).
+  constexpr int kLanesPerRow = C::kWTN / 8;     // epilogue passes: 8 consecutive columns a lane
   constexpr int kRowsPerPass = 64 / kLanesPerRow;
   constexpr int kPasses = 32 / kRowsPerPass;
-  // Tall apply and polynomial: the epilogue operand (X[i][j], A[i][j]) of this wave's block is its
-  // P operand at k = j, and it passes through the wave's registers as MFMA fragments while the k
-  // loop crosses the wave's columns (k-steps xs0 .. xs0 + kXsKs - 1).  Those fragments of its
-  // kXsFm 32-row blocks (all of them) are kept, 32 registers for a 64x64 wave block, and the
-  // epilogue takes the operand from them instead of reading it again from memory (for the apply
-  // X has left L2 by then: one mlp apply re-read ~90 MB of it from HBM).
-  constexpr int kXsFm = (OP == OP_APPLY_XT || OP == OP_POLY) ? C::kFM : 0;
-  constexpr int kXsKs = C::kWTN / 16;
-  const int xs0 = (j0 + wn * C::kWTN) / 16;
-  bf16x8_t xs[kXsFm > 0 ? kXsKs : 1][kXsFm > 0 ? kXsFm : 1];
-  if constexpr (kXsFm > 0) {
+  constexpr bool kKeep = OP != OP_GRAM;
+  constexpr bool kXsQ = OP == OP_APPLY;
+  constexpr int kXsKs = kXsQ ? C::kWTM / 16 : C::kWTN / 16;   // k-steps kept
+  constexpr int kXsF = kXsQ ? C::kFN : C::kFM;                 // fragments kept per k-step
+  const int xs0 = kXsQ ? (i0 + wm * C::kWTM) / 16 : (j0 + wn * C::kWTN) / 16;
+  bf16x8_t xs[kKeep ? kXsKs : 1][kKeep ? kXsF : 1];
+  if constexpr (kKeep) {
 #pragma unroll
     for (int q = 0; q < kXsKs; ++q)
 #pragma unroll
-      for (int fm = 0; fm < kXsFm; ++fm) xs[q][fm] = bf16x8_t{};
+      for (int f = 0; f < kXsF; ++f) xs[q][f] = bf16x8_t{};
   }
-  constexpr bool kHasE = OP != OP_GRAM && kXsFm < C::kFM;   // some blocks read E from memory
-  const uint16_t* Eb = p.E ? p.E + b * p.strideE : nullptr;
-  u32x4_t ecur[kHasE ? kPasses : 1];
-  auto load_e = [&](u32x4_t* dst, int fm) {
-#pragma unroll
-    for (int pass = 0; pass < kPasses; ++pass) {
-      const int gi = i0 + wm * C::kWTM + fm * 32 + pass * kRowsPerPass + lane / kLanesPerRow;
-      const int gj = j0 + wn * C::kWTN + (lane % kLanesPerRow) * 8;
-      dst[pass] = (gi < p.M && gj < p.N)
-                      ? *reinterpret_cast<const u32x4_t*>(Eb + (int64_t)gi * p.lde + gj)
-                      : u32x4_t{0u, 0u, 0u, 0u};
-    }
-  };
 
   // On a diagonal tile of a symmetric product, a wave whose block lies wholly below the diagonal
   // stores nothing (those entries come from the mirror of the block above it): it takes its share
@@ -534,9 +520,6 @@ void gemm_kernel(GemmParams p) {
       }
     }
     if (kPadded && kt >= KT) continue;
-    if constexpr (kHasE) {
-      if (kt == KT - 1) load_e(ecur, kXsFm);
-    }
     if (idle) continue;
     const char* tp = smem + ((kt - kt0) % STAGES) * C::kStageBytes;
     const char* tq = same_pq ? tp : tp + C::kQOffset;
@@ -581,7 +564,7 @@ void gemm_kernel(GemmParams p) {
         // keep the reads ahead of the multiplies (the scheduler would sink each to its use)
         if constexpr (kHoist) __builtin_amdgcn_sched_barrier(0);
       }
-      if constexpr (kXsFm > 0) {
+      if constexpr (kKeep) {
         const int aks = kt * kKs + ks;
 #pragma unroll
         for (int q = 0; q < kXsKs; ++q)
@@ -589,7 +572,13 @@ void gemm_kernel(GemmParams p) {
             // a real branch (taken on a few slabs): keeps the copies out of the other slabs
             asm volatile("" ::: "memory");
 #pragma unroll
-            for (int fm = 0; fm < kXsFm; ++fm) xs[q][fm] = fa[ks][fm];
+            for (int f = 0; f < kXsF; ++f) {
+              if constexpr (kXsQ) {
+                xs[q][f] = fb[ks][f];
+              } else {
+                xs[q][f] = fa[ks][f];
+              }
+            }
           }
       }
 #pragma unroll
@@ -674,25 +663,53 @@ void gemm_kernel(GemmParams p) {
 #pragma unroll
   for (int fm = 0; fm < C::kFM; ++fm) {
     if (!computes) break;
-    u32x4_t enext[kHasE ? kPasses : 1];
-    if constexpr (kHasE) {
-      if (fm + 1 < C::kFM && fm + 1 > kXsFm) load_e(enext, fm + 1);
-    }
-    // A kept block's X: lane l holds row l%32 at k = 16q + 8(l/32) + 0..7 of k-step q, while its
-    // accumulator holds columns 8q' + 4(l/32) + 0..3 of each 32-column fragment.  Swapping dwords
-    // 2, 3 of the lower 32 lanes with dwords 0, 1 of the upper 32 leaves every lane with its own
-    // columns: dwords 0, 1 of k-step 2fn + q'/2 for even q', dwords 2, 3 for odd q'.
-    u32x4_t xw[kXsFm > 0 ? kXsKs : 1];
-    if constexpr (kXsFm > 0) {
-      if (fm < kXsFm) {
+    // The kept operand of this block in the accumulators' layout: lane l needs entries
+    // (row l%32, columns 8q' + 4(l/32) + 0..3) of every 32-column fragment fn, as two dwords
+    // xw[fn][q'].
+    u32x2_t xw[kKeep ? C::kFN : 1][4];
+    if constexpr (kKeep && !kXsQ) {
+      // P fragments: lane l holds row l%32 at k = 16q + 8(l/32) + 0..7 of k-step q.  Swapping
+      // dwords 2, 3 of the lower 32 lanes with dwords 0, 1 of the upper 32 leaves every lane
+      // with its own columns: dwords 0, 1 of k-step 2fn + q'/2 for even q', dwords 2, 3 for odd.
 #pragma unroll
-        for (int q = 0; q < kXsKs; ++q) {
-          const u32x4_t w = __builtin_bit_cast(u32x4_t, xs[q][fm]);
-          const auto s02 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
-          const auto s13 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
-          xw[q] = u32x4_t{s02[0], s13[0], s02[1], s13[1]};
-        }
+      for (int q = 0; q < kXsKs; ++q) {
+        const u32x4_t w = __builtin_bit_cast(u32x4_t, xs[q][fm]);
+        const auto s02 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+        const auto s13 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+        xw[q / 2][2 * (q % 2)] = u32x2_t{s02[0], s13[0]};
+        xw[q / 2][2 * (q % 2) + 1] = u32x2_t{s02[1], s13[1]};
       }
+    } else if constexpr (kXsQ) {
+      // Q fragments (wide apply): lane l holds column 32fn + l%32 at rows 16q + 8(l/32) + 0..7
+      // of k-step q.  The block's two k-steps go to LDS as rows of 32 bf16 per column (column
+      // c at byte c * kXP), and transposing reads bring back rows: in each 16-lane group g,
+      // lane 4a + b points at columns 8q' + 4(g/2) + a, rows 16(g%2) + 4b .. +3, and lane r
+      // receives those four columns of row 16(g%2) + r (a 96-byte pitch spreads both the
+      // 16-byte writes and the 8-byte reads evenly over the banks).
+      constexpr int kXP = 96;
+      static_assert(C::kWTN * kXP <= 32 * C::kEpiPitch * 4, "transpose fits the wave's area");
+      char* xt = reinterpret_cast<char*>(epi);
+#pragma unroll
+      for (int fn = 0; fn < C::kFN; ++fn)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          *reinterpret_cast<u32x4_t*>(xt + (fn * 32 + (lane & 31)) * kXP +
+                                      (16 * h + 8 * (lane >> 5)) * 2) =
+              __builtin_bit_cast(u32x4_t, xs[2 * fm + h][fn]);
+      wait_lds();
+      __builtin_amdgcn_wave_barrier();
+      const int g = lane >> 4;
+      const int r = lane & 15;
+#pragma unroll
+      for (int fn = 0; fn < C::kFN; ++fn)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          xw[fn][q] = __builtin_bit_cast(
+              u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(
+                           xt + (fn * 32 + 8 * q + 4 * (g >> 1) + (r >> 2)) * kXP +
+                           (16 * (g & 1) + 4 * (r & 3)) * 2)));
+      wait_lds();   // the staging below overwrites the area
+      __builtin_amdgcn_wave_barrier();
     }
 #pragma unroll
     for (int fn = 0; fn < C::kFN; ++fn)
@@ -702,20 +719,18 @@ void gemm_kernel(GemmParams p) {
         const int col = fn * 32 + 8 * q + 4 * (lane >> 5);
         float v[4] = {acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1], acc[fm][fn][4 * q + 2],
                       acc[fm][fn][4 * q + 3]};
-        if constexpr (kXsFm > 0) {
-          if (fm < kXsFm) {
-            // the epilogue expressions of the direct pass and of the polynomial's combine below
-            const u32x4_t w = xw[2 * fn + q / 2];
+        if constexpr (kKeep) {
+          // the epilogue expression in fp32: b A + c (A A) for the polynomial; a X + P, or
+          // bf16(P) + a X with split rounding, for the apply
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const uint32_t d = w[2 * (q % 2) + e / 2];
-              const float ax = p.alpha * bf16_to_f32((e % 2) ? (d >> 16) : (d & 0xFFFFu));
-              if constexpr (OP == OP_POLY) {
-                const float cq = p.beta * v[e];
-                v[e] = ax + cq;
-              } else {
-                v[e] = p.split ? bf16_to_f32(f32_to_bf16(v[e])) + ax : ax + v[e];
-              }
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t d = xw[fn][q][e / 2];
+            const float ax = p.alpha * bf16_to_f32((e % 2) ? (d >> 16) : (d & 0xFFFFu));
+            if constexpr (OP == OP_POLY) {
+              const float cq = p.beta * v[e];
+              v[e] = ax + cq;
+            } else {
+              v[e] = p.split ? bf16_to_f32(f32_to_bf16(v[e])) + ax : ax + v[e];
             }
           }
         }
@@ -726,36 +741,6 @@ void gemm_kernel(GemmParams p) {
 
     const int gi0 = i0 + wm * C::kWTM + fm * 32;   // first global row of this block
     const int gj0 = j0 + wn * C::kWTN;             // first global col of this wave
-
-
-    if constexpr (OP == OP_POLY && kHasE) {
-      // B = b*A + c*(A*A) for a block without kept A: every piece of the block is combined in LDS
-      // first, so that the stores below (a diagonal tile's transposed reads and the mirror
-      // included) read finished values
-#pragma unroll
-      for (int pass = 0; pass < (fm < kXsFm ? 0 : kPasses); ++pass) {
-        const int row = pass * kRowsPerPass + lane / kLanesPerRow;
-        const int col = (lane % kLanesPerRow) * 8;
-        if (gi0 + row >= p.M || gj0 + col >= p.N) continue;
-        const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(ep(row, col));
-        const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(ep(row, col + 4));
-        float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        const u32x4_t ae = ecur[pass];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float ba0 = p.alpha * bf16_to_f32(ae[e] & 0xFFFFu);
-          const float ba1 = p.alpha * bf16_to_f32(ae[e] >> 16);
-          const float cq0 = p.beta * v[2 * e];
-          const float cq1 = p.beta * v[2 * e + 1];
-          v[2 * e] = ba0 + cq0;
-          v[2 * e + 1] = ba1 + cq1;
-        }
-        *reinterpret_cast<f32x4_t*>(ep(row, col)) = f32x4_t{v[0], v[1], v[2], v[3]};
-        *reinterpret_cast<f32x4_t*>(ep(row, col + 4)) = f32x4_t{v[4], v[5], v[6], v[7]};
-      }
-      wait_lds();
-      __builtin_amdgcn_wave_barrier();
-    }
 
     // direct rows: each lane takes 8 consecutive columns of one row
 #pragma unroll
@@ -770,28 +755,9 @@ void gemm_kernel(GemmParams p) {
       float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
       u32x4_t out;
       if constexpr (kApply) {
-        if (fm < kXsFm) {
-          // a kept block is already a·X + P (or its split form) in fp32
+        // already a·X + P (or its split form) in fp32
 #pragma unroll
-          for (int e = 0; e < 4; ++e) out[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
-          *reinterpret_cast<u32x4_t*>(Cb + (int64_t)gi * p.ldc + gj) = out;
-          continue;
-        }
-        const u32x4_t xe = ecur[kHasE ? pass : 0];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float ax0 = p.alpha * bf16_to_f32(xe[e] & 0xFFFFu);
-          const float ax1 = p.alpha * bf16_to_f32(xe[e] >> 16);
-          float r0, r1;
-          if (p.split) {
-            r0 = bf16_to_f32(f32_to_bf16(v[2 * e])) + ax0;
-            r1 = bf16_to_f32(f32_to_bf16(v[2 * e + 1])) + ax1;
-          } else {
-            r0 = ax0 + v[2 * e];
-            r1 = ax1 + v[2 * e + 1];
-          }
-          out[e] = pack_bf16x2(r0, r1);
-        }
+        for (int e = 0; e < 4; ++e) out[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
         *reinterpret_cast<u32x4_t*>(Cb + (int64_t)gi * p.ldc + gj) = out;
       } else {
         if (diag_tile) {
@@ -854,12 +820,6 @@ void gemm_kernel(GemmParams p) {
     }
     wait_lds();
     __builtin_amdgcn_wave_barrier();
-    if constexpr (kHasE) {
-      if (fm + 1 < C::kFM && fm + 1 > kXsFm) {
-#pragma unroll
-        for (int pass = 0; pass < kPasses; ++pass) ecur[pass] = enext[pass];
-      }
-    }
   }
 
   if constexpr (OP == OP_GRAM) {
@@ -916,7 +876,6 @@ hipError_t launch(GemmParams p, int64_t g, hipStream_t stream) {
     q.P += b0 * p.strideP;
     q.Q += b0 * p.strideQ;
     q.C += b0 * p.strideC;
-    if (q.E) q.E += b0 * p.strideE;
     if (q.trace) q.trace += b0 * p.trace_slots;
     q.total = (int)(p.tiles * gb);
     // Gram launches of one to two rounds whose diagonal tiles can fill every shared CU (the Vs
@@ -1309,9 +1268,6 @@ hipError_t launch_poly(const uint16_t* a, uint16_t* bout, float coef_b, float co
   p.C = bout;
   p.strideC = (int64_t)s * s;
   p.ldc = s;
-  p.E = a;
-  p.strideE = (int64_t)s * s;
-  p.lde = s;
   p.alpha = coef_b;
   p.beta = coef_c;
   p.tiles_m = p.tiles_n = ceil_div(s, poly_tile(s));
@@ -1360,7 +1316,7 @@ hipError_t launch_apply_tall(const uint16_t* x, const uint16_t* bm, uint16_t* c,
 }
 
 // Wide (and square) apply, C = a X + B X: P = rows of B (K = m contiguous), Q(j, k) = X[k][j]
-// (K-major); the epilogue reads a X[i][j] from memory.
+// (K-major); the epilogue takes X[i][j] from the Q fragments its waves keep.
 template <int BM, int BN, int WM, int WN, int STAGES, int BK>
 hipError_t launch_apply_wide(const uint16_t* x, const uint16_t* bm, uint16_t* c, float coef_a,
                              bool split, const Shape& sh, hipStream_t stream) {
@@ -1380,9 +1336,6 @@ hipError_t launch_apply_wide(const uint16_t* x, const uint16_t* bm, uint16_t* c,
   p.C = c;
   p.strideC = (int64_t)sh.m * sh.n;
   p.ldc = sh.n;
-  p.E = x;
-  p.strideE = (int64_t)sh.m * sh.n;
-  p.lde = sh.n;
   p.alpha = coef_a;
   p.split = split ? 1 : 0;
   p.tiles_m = ceil_div(p.M, BM);
