@@ -17,9 +17,10 @@
 //          wide: C = a X + B X   (P = B, Q(j, k) = X[k][j]: K-major)
 //          epilogue bf16(a * X[i][j] + acc), or with split rounding
 //          bf16(bf16(acc) + a * X[i][j]) (the page's two-kernel form for banks of > 1024 rows).
-//          The tall apply's X[i][j] is its own P operand at k = j: each wave keeps the MFMA
-//          fragments of X that cover its columns as the k loop passes them, and its epilogue
-//          loads nothing from memory.
+//
+// No epilogue reads its operand from memory: the polynomial's A[i][j] and the tall apply's
+// X[i][j] are their P operand at k = j, the wide apply's X[i][j] its Q operand at k = i, and each
+// wave keeps the MFMA fragments that hold them for its block as the k loop passes them.
 //
 // The Gram and the polynomial are symmetric: only tiles on or above the diagonal are computed,
 // and each is stored twice (C[i][j] and C[j][i]) from the same fp32 value, so the stored matrices
